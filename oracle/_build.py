@@ -1,0 +1,48 @@
+"""Build the CPU oracle (test infrastructure) and the shared input generator.
+
+synth/synth.o is compiled once with gcc and linked into BOTH the oracle and the
+HIP library, so the two sides draw bit-identical synthetic inputs.  The oracle
+itself is plain C built with gcc -O3 and no fast-math (the pages' default flags:
+openai.wiki "llama2.c | Baby LLaMA", section "Performance optimisation").
+"""
+import os
+import subprocess
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SYNTH_SRC = os.path.join(ROOT, "synth", "synth.c")
+SYNTH_OBJ = os.path.join(ROOT, "synth", "synth.o")
+ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
+ORACLE_LIB = os.path.join(ROOT, "oracle", "liboracle.so")
+
+CFLAGS = ["-O3", "-fPIC", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("command failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
+
+
+def build_synth():
+    _run(["gcc", "-O2", "-fPIC", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+          "-c", SYNTH_SRC, "-o", SYNTH_OBJ])
+    return SYNTH_OBJ
+
+
+def build_oracle(src=ORACLE_SRC, out=ORACLE_LIB, extra=()):
+    """Compile an oracle source (the real one, or a planted-mistake copy made by a test)."""
+    if not os.path.exists(SYNTH_OBJ):
+        build_synth()
+    _run(["gcc", *CFLAGS, *extra, "-I", os.path.join(ROOT, "oracle"), "-I", os.path.join(ROOT, "synth"), "-shared",
+          "-Wl,-Bsymbolic", src, SYNTH_OBJ, "-o", out, "-lm", "-lpthread"])
+    return out
+
+
+def build():
+    build_synth()
+    build_oracle()
+
+
+if __name__ == "__main__":
+    build()
+    print(ORACLE_LIB)

@@ -1,0 +1,137 @@
+/*
+ * ld.h -- C ABI of the MI355X (gfx950) fp32 Llama-2-architecture decode library.
+ *
+ * The operation: greedy autoregressive decoding of a Llama-2-architecture
+ * transformer held in fp32, one forward pass per position, as the pages' single
+ * C-file engine does on a CPU (openai.wiki "llama2.c | Baby LLaMA", intro and
+ * section "Model inference"; Xinzhiyuan's llama2.c report, sections "Feel the
+ * magic" and "Usage").  One forward pass over a position runs: token embedding,
+ * then per layer RMSNorm -> Q/K/V projections -> rotary embedding -> causal
+ * attention over the KV cache -> output projection + residual -> RMSNorm ->
+ * SwiGLU FFN + residual; then a final RMSNorm, the classifier (tied to the
+ * embedding unless configured otherwise) and a greedy arg-max.  The pages give
+ * no equations; each step follows its published definition (RMSNorm: Zhang &
+ * Sennrich 2019 eq. 4; rotary embedding: Su et al. 2021 eq. 34 with adjacent
+ * pairs; SwiGLU: Shazeer 2020 sec. 2; block layout: Touvron et al. 2023 sec. 2.2).
+ * Decoding stops at max_seq positions, as the pages' TODO about running past
+ * max_seq_len says (openai.wiki "llama2.c | Baby LLaMA", "Unsorted TODO").
+ *
+ * Conventions for every call:
+ *  - Return LD_OK (0) or a negative LD_E_* code.  On error no state changes.
+ *  - `hip_stream` passed to ld_model_init is used for every later call; all
+ *    calls except ld_model_init, ld_read_weights, ld_status and
+ *    ld_profile_read are asynchronous on that stream and never allocate.
+ *  - Device memory is owned by the caller: one arena of ld_arena_bytes() bytes
+ *    (256-byte aligned) holds weights, rotary tables, KV cache and scratch.
+ *    Output buffers (logits, next tokens) are caller-owned device memory.
+ *  - All sequences of a batch share one position counter (lockstep decoding).
+ *  - A handle is not thread-safe; separate handles are independent.
+ *  - Tensors are fp32, token ids int32, matrices row-major [out][in].
+ */
+#ifndef LD_H
+#define LD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LD_OK 0
+#define LD_E_INVAL -1     /* bad argument: config, batch, token id, NULL pointer */
+#define LD_E_RANGE -2     /* position would pass max_seq */
+#define LD_E_ARENA -3     /* arena too small or misaligned */
+#define LD_E_HIP -4       /* a HIP runtime call failed */
+#define LD_E_NONFINITE -5 /* a logit was NaN or infinite, or a device token was out of range */
+#define LD_E_STATE -6     /* call not valid in the handle's state */
+
+typedef struct {
+  int32_t dim;             /* model width d; multiple of 32 */
+  int32_t n_layers;        /* L */
+  int32_t n_heads;         /* H; head_dim = dim / n_heads, a multiple of 16, <= 256 */
+  int32_t hidden_dim;      /* SwiGLU width f; multiple of 32 */
+  int32_t vocab_size;      /* V */
+  int32_t max_seq;         /* positions held by the KV cache */
+  int32_t max_batch;       /* sequences decoded in lockstep, >= 1 */
+  int32_t tied_classifier; /* 1: classifier = token embedding; 0: separate matrix */
+  double rope_theta;       /* rotary base, 10000 for Llama-2 */
+  double norm_eps;         /* RMSNorm epsilon, added inside the square root */
+} ld_config;
+
+typedef struct ld_model ld_model;
+
+/* Device bytes the arena must hold for `cfg`.  LD_E_INVAL for an unsupported
+ * config (see the field comments). */
+int ld_arena_bytes(const ld_config* cfg, size_t* bytes_out);
+
+/* Build a model in `dev_arena`: draw every weight from `seed` with the shared
+ * synthetic generator (N(0, 0.02) per element, gains 1.0; stream layout in
+ * synth/synth.h), upload, fill the rotary tables, zero the KV cache, set the
+ * position to 0.  Synchronous.  `hip_stream` is a hipStream_t (NULL = default
+ * stream).  *out receives a library-owned handle; free it with ld_model_free
+ * (the arena is never freed by the library). */
+int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t arena_bytes,
+                  void* hip_stream, ld_model** out);
+
+/* Prompt processing: run positions pos .. pos+n_tokens-1 of `batch` sequences
+ * whose token ids are host_tokens[batch][n_tokens] (host memory, validated:
+ * 0 <= id < vocab_size).  Fills the KV cache for those positions; writes the
+ * last position's logits to dev_logits[batch][V] (or every position's to
+ * dev_logits[batch][n_tokens][V] when all_pos != 0; NULL = not written) and
+ * the greedy next token of each sequence to dev_next[batch] (NULL = not
+ * written).  Then pos += n_tokens.  LD_E_RANGE if pos + n_tokens > max_seq. */
+int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host_tokens,
+               float* dev_logits, int32_t* dev_next, int32_t all_pos);
+
+/* One decode position for `batch` sequences.  tokens[batch] are host token ids
+ * (validated) or, when tokens_on_device != 0, a device array (e.g. the
+ * previous step's dev_next; an out-of-range device id is replaced by 0 and
+ * reported by ld_status as LD_E_NONFINITE).  Writes logits [batch][V] to
+ * dev_logits (NULL = not written) and the greedy tokens (lowest index among
+ * equal maxima) to dev_next (NULL = not written).  Then pos += 1. */
+int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
+                   float* dev_logits, int32_t* dev_next);
+
+/* Forget the cached sequence: pos := 0. */
+int ld_kv_reset(ld_model* m);
+
+/* Rewind: pos := new_pos, 0 <= new_pos <= current pos (positions >= new_pos
+ * are recomputed by later calls). */
+int ld_set_pos(ld_model* m, int32_t new_pos);
+
+int ld_get_pos(const ld_model* m, int32_t* pos);
+
+/* Copy elements [start, start+n) of weight tensor `stream_id` (synth stream
+ * numbering, logical row-major layout) to host memory.  Synchronous. */
+int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, float* host_out);
+
+/* Wait for the stream and report a device-side error raised since the last
+ * call (LD_E_NONFINITE), then clear it. */
+int ld_status(ld_model* m);
+
+/* Kernel timing with HIP events recorded on the model's stream around every
+ * launch of one kernel class (LD_K_*), for measuring a kernel inside a real
+ * run.  ld_profile_read waits for the stream, returns the mean duration in
+ * milliseconds and the count of launches recorded since enabling, and resets. */
+#define LD_K_QKV 0
+#define LD_K_ATTN 1
+#define LD_K_WO 2
+#define LD_K_W13 3
+#define LD_K_W2 4
+#define LD_K_CLS 5
+#define LD_K_COUNT 6
+int ld_profile(ld_model* m, int32_t kernel_class, int32_t enable);
+int ld_profile_read(ld_model* m, int32_t kernel_class, double* avg_ms, int64_t* count);
+
+/* Synthetic prompt tokens from the shared generator (uniform on [lo, hi)). */
+int ld_synth_prompt(uint64_t seed, uint64_t seq, int32_t n, int32_t lo, int32_t hi,
+                    int32_t* host_out);
+
+void ld_model_free(ld_model* m);
+const char* ld_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,20 +1,32 @@
-"""Build the CPU oracle (test infrastructure) and the shared input generator.
+"""Build the CPU oracle (test infrastructure).
 
-synth/synth.o is compiled once with gcc and linked into BOTH the oracle and the
-HIP library, so the two sides draw bit-identical synthetic inputs.  The oracle
-itself is plain C built with gcc -O3 and no fast-math (the pages' default flags:
-openai.wiki "llama2.c | Baby LLaMA", section "Performance optimisation").
+The oracle is plain C built with gcc -O3 and no fast-math (the pages' default
+flags: openai.wiki "llama2.c | Baby LLaMA", section "Performance optimisation"),
+linked with the shared input generator object synth/synth.o.
 """
+import importlib.util
 import os
 import subprocess
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SYNTH_SRC = os.path.join(ROOT, "synth", "synth.c")
-SYNTH_OBJ = os.path.join(ROOT, "synth", "synth.o")
 ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
 ORACLE_LIB = os.path.join(ROOT, "oracle", "liboracle.so")
 
 CFLAGS = ["-O3", "-fPIC", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
+
+
+def _synth():
+    spec = importlib.util.spec_from_file_location("synth_build", os.path.join(ROOT, "synth", "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+SYNTH_OBJ = _synth().OBJ
+
+
+def build_synth():
+    return _synth().build_synth()
 
 
 def _run(cmd):
@@ -23,18 +35,12 @@ def _run(cmd):
         raise RuntimeError("command failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
 
 
-def build_synth():
-    _run(["gcc", "-O2", "-fPIC", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall",
-          "-c", SYNTH_SRC, "-o", SYNTH_OBJ])
-    return SYNTH_OBJ
-
-
 def build_oracle(src=ORACLE_SRC, out=ORACLE_LIB, extra=()):
     """Compile an oracle source (the real one, or a planted-mistake copy made by a test)."""
     if not os.path.exists(SYNTH_OBJ):
         build_synth()
-    _run(["gcc", *CFLAGS, *extra, "-I", os.path.join(ROOT, "oracle"), "-I", os.path.join(ROOT, "synth"), "-shared",
-          "-Wl,-Bsymbolic", src, SYNTH_OBJ, "-o", out, "-lm", "-lpthread"])
+    _run(["gcc", *CFLAGS, *extra, "-I", os.path.join(ROOT, "oracle"), "-I", os.path.join(ROOT, "synth"),
+          "-shared", "-Wl,-Bsymbolic", src, SYNTH_OBJ, "-o", out, "-lm", "-lpthread"])
     return out
 
 

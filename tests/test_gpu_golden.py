@@ -1,0 +1,133 @@
+"""GPU parity at the full workload sizes, against stored oracle outputs.
+
+tests/golden/<workload>.npz are written by tests/golden/make_golden.py, which
+calls only the oracle: for every stored sequence and position, the token fed
+in (the oracle's own greedy stream, used here for teacher forcing), the greedy
+token out, the top-1 and top-2 logit values, and full logit vectors at a few
+positions.  The GPU runs the workload in the configuration the benchmark times
+(prefill of the prompt, then lockstep decode steps) and is checked on:
+  * every logit at the stored positions (tolerance of tests/parity.py);
+  * at every position: the GPU logit at the oracle's arg-max index against the
+    oracle's top-1 value, and the greedy token where the oracle's top-1 margin
+    exceeds 1e-3.
+"""
+import hashlib
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from transformer_llama_decode_amd.configs import WORKLOADS
+from tests.parity import REL, ABS, MARGIN, assert_logits
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = os.path.join(ROOT, "tests", "golden")
+SOURCES = ["oracle/oracle.c", "oracle/oracle.h", "synth/synth.c", "synth/synth.h"]
+
+
+def _say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _golden(name):
+    path = os.path.join(GOLD, "%s.npz" % name)
+    if not os.path.exists(path):
+        pytest.skip("no stored oracle outputs for %s (run tests/golden/make_golden.py %s)" % (name, name))
+    z = np.load(path, allow_pickle=False)
+    assert str(z["source_hash"]) == _source_hash(), "stored oracle outputs are stale: regenerate"
+    return z
+
+
+def _run(name, gold_name=None, seqs=None):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_llama_decode_amd.model import LlamaDecoder
+    w = WORKLOADS[name]
+    z = _golden(gold_name or name)
+    allseqs = list(z["seqs"])
+    rows = [allseqs.index(s) for s in (seqs if seqs is not None else allseqs)]
+    B = len(rows)
+    tin, greedy = z["tokens_in"][rows], z["greedy"][rows]
+    top1, top2 = z["top1"][rows], z["top2"][rows]
+    full = {(int(s), int(p)): z["full_logits"][i] for i, (s, p) in enumerate(zip(z["full_seq"], z["full_pos"]))}
+    seq_ids = [allseqs[r] for r in rows]
+    dev = torch.device("cuda", 0)
+    _say("%s: init model (B=%d)" % (name, B))
+    gm = LlamaDecoder(w.model, w.model_seed)
+    V = w.model.vocab_size
+    P = max(w.prompt_len, 1)
+    logits = torch.empty((B, V), dtype=torch.float32, device=dev)
+    idx_top = torch.from_numpy(greedy.astype(np.int64)).to(dev)      # [B, E]
+    ar = torch.arange(B, device=dev)
+    fails = []
+
+    def check(p, nxt):
+        got_top = logits[ar, idx_top[:, p]].cpu().numpy().astype(np.float64)
+        want = top1[:, p].astype(np.float64)
+        bad = np.abs(got_top - want) > np.maximum(REL * np.abs(want), ABS)
+        if bad.any():
+            fails.append("pos %d: top-1 value off for %d seqs" % (p, int(bad.sum())))
+        nn = nxt.cpu().numpy()
+        margin = top1[:, p] - top2[:, p]
+        wrong = (margin > MARGIN) & (nn != greedy[:, p])
+        if wrong.any():
+            fails.append("pos %d: greedy token differs for %d seqs" % (p, int(wrong.sum())))
+        for bi, s in enumerate(seq_ids):
+            if (s, p) in full:
+                assert_logits(logits[bi].cpu().numpy(), full[(s, p)], "%s seq %d pos %d" % (name, s, p))
+
+    if w.prompt_len > 0:
+        _say("%s: prefill %d x %d" % (name, B, P))
+        nxt = gm.prefill(tin[:, :P], logits=logits)
+        check(P - 1, nxt)
+    for p in range(P if w.prompt_len > 0 else 0, w.end_pos):
+        nxt = gm.decode_step(np.ascontiguousarray(tin[:, p]), logits=logits)
+        check(p, nxt)
+        if p % 128 == 0:
+            _say("%s: pos %d" % (name, p))
+    assert gm.status() == 0
+    gm.close()
+    assert not fails, fails[:10]
+
+
+def test_golden_C1():
+    _run("C1")
+
+
+def test_golden_C2():
+    _run("C2")
+
+
+def test_golden_C3_batch256():
+    _run("C3")
+
+
+def test_golden_C4_batch1():
+    # batch 1 of the 110M shape is sequence 0 of the batch-32 run
+    from dataclasses import replace
+    WORKLOADS["_C4b1"] = replace(WORKLOADS["C4"], name="_C4b1")
+    try:
+        _run("_C4b1", gold_name="C4b32", seqs=[0])
+    finally:
+        del WORKLOADS["_C4b1"]
+
+
+def test_golden_C4_batch32():
+    _run("C4b32")
+
+
+@pytest.mark.timeout(900)
+def test_golden_C5():
+    _run("C5")

@@ -1,0 +1,99 @@
+"""The C-ABI library loads and exports every entry point of include/ld.h (CPU only).
+
+No compute calls: only the host-side entry points that touch no GPU
+(arena sizing / config validation, the synthetic prompt generator).
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from transformer_llama_decode_amd import _lib
+from transformer_llama_decode_amd.configs import WORKLOADS, TINY, ModelConfig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ld.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from transformer_llama_decode_amd import _build
+        _build.build()
+    return _lib.lib()
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ld_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared()
+    assert names == sorted(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (ld_[a-z_]+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_library_is_built_for_gfx950_only():
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          "--input=" + _lib.LIB_PATH], capture_output=True, text=True)
+    if out.returncode != 0:
+        # shared objects carry the device code in a .hip_fatbin section instead
+        sec = subprocess.run(["readelf", "-S", _lib.LIB_PATH], capture_output=True, text=True).stdout
+        assert ".hip_fatbin" in sec
+        blob = open(_lib.LIB_PATH, "rb").read()
+        assert b"gfx950" in blob
+        assert b"gfx942" not in blob and b"gfx90a" not in blob
+
+
+def _cfg(m, **kw):
+    from transformer_llama_decode_amd.model import _cfg_struct
+    from dataclasses import replace
+    return _cfg_struct(replace(m, **kw))
+
+
+@pytest.mark.parametrize("bad", [dict(dim=100), dict(n_heads=5), dict(hidden_dim=100), dict(vocab_size=0),
+                                 dict(max_seq=0), dict(max_batch=0), dict(rope_theta=0.0),
+                                 dict(dim=64, n_heads=1, hidden_dim=64, vocab_size=10, max_seq=4) | {"n_layers": 0},
+                                 dict(dim=512, n_heads=1)])
+def test_arena_bytes_rejects_unsupported_configs(L, bad):
+    n = C.c_size_t(0)
+    assert L.ld_arena_bytes(C.byref(_cfg(TINY, **bad)), C.byref(n)) == _lib.LD_E_INVAL
+
+
+def test_arena_sizes_of_the_workloads(L):
+    for name, w in WORKLOADS.items():
+        n = C.c_size_t(0)
+        assert L.ld_arena_bytes(C.byref(_cfg(w.model)), C.byref(n)) == 0
+        weights = w.model.n_params() * 4
+        assert weights <= n.value < weights * 1.3 + 3 * 2 ** 30, name
+    n = C.c_size_t(0)
+    L.ld_arena_bytes(C.byref(_cfg(WORKLOADS["C5"].model)), C.byref(n))
+    assert n.value < 40 * 2 ** 30          # 7B shape fits one 288 GB MI355X many times over
+
+
+def test_null_arguments_are_rejected(L):
+    assert L.ld_arena_bytes(None, None) == _lib.LD_E_INVAL
+    assert L.ld_kv_reset(None) == _lib.LD_E_INVAL
+    assert L.ld_decode_step(None, 1, None, 0, None, None) == _lib.LD_E_INVAL
+    assert L.ld_prefill(None, 1, 1, None, None, None, 0) == _lib.LD_E_INVAL
+    h = C.c_void_p()
+    assert L.ld_model_init(C.byref(_cfg(TINY)), 0, None, 0, None, C.byref(h)) == _lib.LD_E_INVAL
+    assert L.ld_strerror(_lib.LD_E_RANGE).decode().startswith("position")
+
+
+def test_prompt_generator_is_the_shared_one(L):
+    from oracle import oracle as O
+    from transformer_llama_decode_amd.model import synth_prompt
+    for seed, seq in [(1, 0), (2, 255), (4, 0)]:
+        assert np.array_equal(synth_prompt(seed, seq, 512), O.synth_prompt(seed, seq, 512))

@@ -1,0 +1,72 @@
+// dev_common.hpp -- small device helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+namespace ld {
+
+constexpr int kWave = 64;
+
+// Butterfly sum across the 64 lanes; every lane ends with the same value and the
+// order of additions is fixed, so results are run-to-run identical.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// (value, index) arg-max step: larger value wins, equal values go to the lower index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+// Arg-max across lanes whose ids differ only in the bits of `mask_bits` (xor pattern).
+__device__ __forceinline__ void wave_argmax(float& v, int& i, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) {
+    float v2 = __shfl_xor(v, off, kWave);
+    int i2 = __shfl_xor(i, off, kWave);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+__device__ __forceinline__ double dot4(const float4 w, double x0, double x1, double x2, double x3,
+                                       double acc) {
+  // products of two fp32 values are exact in fp64, so mul+add == fma here
+  acc = fma((double)w.x, x0, acc);
+  acc = fma((double)w.y, x1, acc);
+  acc = fma((double)w.z, x2, acc);
+  acc = fma((double)w.w, x3, acc);
+  return acc;
+}
+
+// SwiGLU gate in double, rounded once: silu(h1) * h3, silu(z) = z / (1 + e^-z).
+__device__ __forceinline__ float swiglu(float h1, float h3) {
+  double z = (double)h1;
+  return (float)((z / (1.0 + exp(-z))) * (double)h3);
+}
+
+// Rotary rotation of one adjacent pair in double, rounded to fp32.
+__device__ __forceinline__ void rope_pair(float y0, float y1, float c, float s, float& o0,
+                                          float& o1) {
+  double a = y0, b = y1, cc = c, ss = s;
+  o0 = (float)(a * cc - b * ss);
+  o1 = (float)(a * ss + b * cc);
+}
+
+// Index of element (position p, dimension i) in a head's K-cache tiles [Sp/64][hd][64].
+__device__ __forceinline__ size_t ktile_index(int p, int i, int hd) {
+  return ((size_t)(p >> 6) * hd + i) * 64 + (p & 63);
+}
+
+}  // namespace ld

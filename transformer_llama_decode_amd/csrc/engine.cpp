@@ -1,0 +1,750 @@
+// engine.cpp -- host side of the decode library: the C ABI of include/ld.h.
+//
+// Owns no device memory: every buffer is carved out of the caller's arena
+// (one-shot 1-D memory layout, as the llm.c piece describes its training code:
+// "allocate everything once at start, then stream batches through"), so the
+// steady state never calls hipMalloc.  The forward pass is a fixed sequence of
+// kernel launches on the caller's stream; batch 1 uses the HBM-streaming GEMV
+// kernels, more rows use the MFMA GEMM kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "ld_internal.hpp"
+#include "synth.h"
+
+using namespace ld;
+
+namespace {
+
+constexpr int kMaxRowsCap = 4096;     // activation rows per forward pass (prefill is chunked)
+constexpr int kTokSlots = 4;          // pinned host slots for host token ids
+constexpr int kProfPairs = 8192;      // event pairs per profiled kernel class
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int validate(const ld_config* c) {
+  if (c == nullptr) return LD_E_INVAL;
+  if (c->dim <= 0 || c->dim % 32 != 0 || c->dim > 16384) return LD_E_INVAL;
+  if (c->n_layers <= 0 || c->n_layers > 1024) return LD_E_INVAL;
+  if (c->n_heads <= 0 || c->dim % c->n_heads != 0) return LD_E_INVAL;
+  const int hd = c->dim / c->n_heads;
+  if (hd % 16 != 0 || hd > 256) return LD_E_INVAL;
+  if (c->hidden_dim <= 0 || c->hidden_dim % 32 != 0 || c->hidden_dim > 65536) return LD_E_INVAL;
+  if (c->vocab_size <= 0 || c->vocab_size > (1 << 20)) return LD_E_INVAL;
+  if (c->max_seq <= 0 || c->max_seq > (1 << 16)) return LD_E_INVAL;
+  if (c->max_batch <= 0 || c->max_batch > 4096) return LD_E_INVAL;
+  if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0)) return LD_E_INVAL;
+  return LD_OK;
+}
+
+void make_layout(const ld_config* c, Layout* L) {
+  const size_t d = c->dim, f = c->hidden_dim, V = c->vocab_size, NL = c->n_layers,
+               H = c->n_heads, hd = d / H, S = c->max_seq, B = c->max_batch;
+  const size_t Sp = round_up(S, 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += round_up(bytes, kAlign);
+    return o;
+  };
+  L->E = take(V * d * 4);
+  L->o_wqkv = 0;
+  L->o_wo = L->o_wqkv + round_up(3 * d * d * 4, kAlign);
+  L->o_w13 = L->o_wo + round_up(d * d * 4, kAlign);
+  L->o_w2 = L->o_w13 + round_up(2 * f * d * 4, kAlign);
+  L->o_gatt = L->o_w2 + round_up(d * f * 4, kAlign);
+  L->o_gffn = L->o_gatt + round_up(d * 4, kAlign);
+  L->layer_stride = L->o_gffn + round_up(d * 4, kAlign);
+  L->layer0 = take(L->layer_stride * NL);
+  L->Wcls = c->tied_classifier ? L->E : take(V * d * 4);
+  L->gain_final = take(d * 4);
+  L->rope_cos = take(S * (hd / 2) * 4);
+  L->rope_sin = take(S * (hd / 2) * 4);
+  L->Kc = take(NL * B * H * Sp * hd * 4);
+  L->Vc = take(NL * B * H * Sp * hd * 4);
+  const size_t R = std::max(B, std::min((size_t)kMaxRowsCap, B * S));
+  L->rows = (int)R;
+  L->seq_pad = (int)Sp;
+  L->x = take(R * d * 4);
+  L->xn = take(R * d * 4);
+  L->q = take(R * d * 4);
+  L->att = take(R * d * 4);
+  L->g = take(R * f * 4);
+  L->attn_part = take((size_t)kMaxAttnParts * (hd + 2) * 8);
+  L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
+  L->arg_val = take(L->arg_parts * 4);
+  L->arg_idx = take(L->arg_parts * 4);
+  L->tok = take(R * 4);
+  L->next = take(R * 4);
+  L->err = take(4);
+  L->total = off;
+}
+
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // start, stop pairs
+  int used = 0;
+};
+
+}  // namespace
+
+struct ld_model {
+  ld_config c;
+  Layout lay;
+  int hd, device;
+  hipStream_t stream;
+  char* arena;
+  int pos;
+  bool carry;
+  int* tok_host[kTokSlots];
+  hipEvent_t tok_ev[kTokSlots];
+  bool tok_ev_live[kTokSlots];
+  int tok_slot;
+  Prof prof[LD_K_COUNT];
+
+  template <typename T>
+  T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
+  float* layer(int l, size_t o) const { return at<float>(lay.layer0 + (size_t)l * lay.layer_stride + o); }
+  float* kc(int l) const {
+    return at<float>(lay.Kc) + (size_t)l * c.max_batch * c.n_heads * lay.seq_pad * hd;
+  }
+  float* vc(int l) const {
+    return at<float>(lay.Vc) + (size_t)l * c.max_batch * c.n_heads * lay.seq_pad * hd;
+  }
+};
+
+namespace {
+
+// Records HIP events around one launch of a profiled kernel class.
+struct ProfScope {
+  Prof* p;
+  hipStream_t s;
+  int idx;
+  ProfScope(ld_model* m, int k) : p(&m->prof[k]), s(m->stream), idx(-1) {
+    if (p->on && p->used < kProfPairs) {
+      idx = p->used++;
+      hipEventRecord(p->ev[2 * idx], s);
+    }
+  }
+  ~ProfScope() {
+    if (idx >= 0) hipEventRecord(p->ev[2 * idx + 1], s);
+  }
+};
+
+#define LD_TRY_HIP(expr)                  \
+  do {                                    \
+    if ((expr) != hipSuccess) return LD_E_HIP; \
+  } while (0)
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) hipSetDevice(dev);
+    else prev = -1;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) hipSetDevice(prev);
+  }
+};
+
+int host_threads() {
+  const char* e = std::getenv("LD_INIT_THREADS");
+  int n = e ? std::atoi(e) : (int)std::thread::hardware_concurrency();
+  if (n < 1) n = 1;
+  if (n > 16) n = 16;
+  return n;
+}
+
+// One piece of host-side weight drawing: n elements of stream `stream`
+// starting at `start` into dst.
+struct Seg {
+  float* dst;
+  uint64_t stream, start;
+  size_t n;
+};
+
+void draw_segments(const std::vector<Seg>& segs, uint64_t seed, int nthreads) {
+  // split into pieces of >= 64K elements and hand them out dynamically
+  std::vector<Seg> pieces;
+  for (const Seg& s : segs) {
+    const size_t piece = 1 << 16;
+    for (size_t o = 0; o < s.n; o += piece)
+      pieces.push_back({s.dst + o, s.stream, s.start + o, std::min(piece, s.n - o)});
+  }
+  std::atomic<size_t> next{0};
+  auto work = [&]() {
+    for (;;) {
+      size_t i = next.fetch_add(1);
+      if (i >= pieces.size()) return;
+      const Seg& p = pieces[i];
+      synth_normal(p.dst, seed, p.stream, p.start, p.n, 0.02);
+    }
+  };
+  std::vector<std::thread> th;
+  for (int t = 1; t < nthreads; ++t) th.emplace_back(work);
+  work();
+  for (auto& t : th) t.join();
+}
+
+// Upload double-buffered through pinned staging memory.
+struct Uploader {
+  hipStream_t s;
+  uint64_t seed;
+  int nthreads;
+  size_t cap;   // floats per staging buffer
+  float* stage[2] = {nullptr, nullptr};
+  hipEvent_t ev[2];
+  bool live[2] = {false, false};
+  int cur = 0;
+  bool ok = true;
+
+  int init() {
+    for (int i = 0; i < 2; ++i) {
+      if (hipHostMalloc((void**)&stage[i], cap * sizeof(float), hipHostMallocDefault) != hipSuccess)
+        return LD_E_HIP;
+      if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) return LD_E_HIP;
+    }
+    return LD_OK;
+  }
+  ~Uploader() {
+    for (int i = 0; i < 2; ++i) {
+      if (live[i]) hipEventSynchronize(ev[i]);
+      if (stage[i]) {
+        hipHostFree(stage[i]);
+        hipEventDestroy(ev[i]);
+      }
+    }
+  }
+  float* acquire() {
+    if (live[cur]) {
+      if (hipEventSynchronize(ev[cur]) != hipSuccess) ok = false;
+      live[cur] = false;
+    }
+    return stage[cur];
+  }
+  void submit(void* dev, size_t nfloats) {
+    if (hipMemcpyAsync(dev, stage[cur], nfloats * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipEventRecord(ev[cur], s) != hipSuccess)
+      ok = false;
+    live[cur] = true;
+    cur ^= 1;
+  }
+  // plain row-major tensor
+  void plain(float* dev, uint64_t stream, size_t n) {
+    for (size_t o = 0; o < n && ok; o += cap) {
+      const size_t cnt = std::min(cap, n - o);
+      float* h = acquire();
+      draw_segments({{h, stream, o, cnt}}, seed, nthreads);
+      submit(dev + o, cnt);
+    }
+  }
+  // W1 (stream s1) and W3 (stream s3), f rows of d each, interleaved in 32-row blocks
+  void w13(float* dev, uint64_t s1, uint64_t s3, size_t f, size_t d) {
+    size_t rows_per = std::max<size_t>(32, (cap / (2 * d)) / 32 * 32);
+    for (size_t r0 = 0; r0 < f && ok; r0 += rows_per) {
+      const size_t nr = std::min(rows_per, f - r0);   // multiple of 32
+      float* h = acquire();
+      std::vector<Seg> segs;
+      for (size_t j = 0; j < nr / 32; ++j) {
+        segs.push_back({h + (2 * j) * 32 * d, s1, (r0 + 32 * j) * d, 32 * d});
+        segs.push_back({h + (2 * j + 1) * 32 * d, s3, (r0 + 32 * j) * d, 32 * d});
+      }
+      draw_segments(segs, seed, nthreads);
+      submit(dev + 2 * r0 * d, 2 * nr * d);
+    }
+  }
+};
+
+int enqueue_host_tokens(ld_model* m, const int32_t* host, size_t n) {
+  const int slot = m->tok_slot;
+  m->tok_slot = (m->tok_slot + 1) % kTokSlots;
+  if (m->tok_ev_live[slot]) {
+    LD_TRY_HIP(hipEventSynchronize(m->tok_ev[slot]));
+    m->tok_ev_live[slot] = false;
+  }
+  std::memcpy(m->tok_host[slot], host, n * sizeof(int32_t));
+  LD_TRY_HIP(hipMemcpyAsync(m->at<int>(m->lay.tok), m->tok_host[slot], n * sizeof(int32_t),
+                            hipMemcpyHostToDevice, m->stream));
+  LD_TRY_HIP(hipEventRecord(m->tok_ev[slot], m->stream));
+  m->tok_ev_live[slot] = true;
+  return LD_OK;
+}
+
+// ---------------------------------------------------------------- forward --
+
+// Batch-1 layers on the GEMV path at position `pos`: the token's embedding is already in x.
+int layers_gemv(ld_model* m, int pos) {
+  const ld_config& c = m->c;
+  const int d = c.dim, f = c.hidden_dim;
+  float* x = m->at<float>(m->lay.x);
+  float* q = m->at<float>(m->lay.q);
+  float* att = m->at<float>(m->lay.att);
+  float* g = m->at<float>(m->lay.g);
+  for (int l = 0; l < c.n_layers; ++l) {
+    {
+      ProfScope ps(m, K_QKV);
+      GemvArgs a{};
+      a.x = x; a.gain = m->layer(l, m->lay.o_gatt); a.eps = c.norm_eps;
+      a.W = m->layer(l, m->lay.o_wqkv); a.N = 3 * d; a.K = d;
+      a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
+      a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
+      a.pos = pos; a.d = d; a.hd = m->hd; a.seq_pad = m->lay.seq_pad;
+      LD_TRY_HIP(launch_gemv_qkv(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_ATTN);
+      AttnArgs a{};
+      a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
+      a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
+      LD_TRY_HIP(launch_attention(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_WO);
+      GemvArgs a{};
+      a.x = att; a.W = m->layer(l, m->lay.o_wo); a.N = d; a.K = d; a.resid = x;
+      LD_TRY_HIP(launch_gemv_resid(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_W13);
+      GemvArgs a{};
+      a.x = x; a.gain = m->layer(l, m->lay.o_gffn); a.eps = c.norm_eps;
+      a.W = m->layer(l, m->lay.o_w13); a.N = f; a.K = d; a.g_out = g;
+      LD_TRY_HIP(launch_gemv_swiglu(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_W2);
+      GemvArgs a{};
+      a.x = g; a.W = m->layer(l, m->lay.o_w2); a.N = d; a.K = f; a.resid = x;
+      LD_TRY_HIP(launch_gemv_resid(a, m->stream));
+    }
+  }
+  return LD_OK;
+}
+
+// rows = B * n_tok rows (sequence-major) on the MFMA GEMM path.
+int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
+  const ld_config& c = m->c;
+  const int d = c.dim, f = c.hidden_dim;
+  float* x = m->at<float>(m->lay.x);
+  float* xn = m->at<float>(m->lay.xn);
+  float* q = m->at<float>(m->lay.q);
+  float* att = m->at<float>(m->lay.att);
+  float* g = m->at<float>(m->lay.g);
+  for (int l = 0; l < c.n_layers; ++l) {
+    LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gatt), rows, d, 1, 0, c.norm_eps,
+                                   m->stream));
+    {
+      ProfScope ps(m, K_QKV);
+      GemmArgs a{};
+      a.A = xn; a.W = m->layer(l, m->lay.o_wqkv); a.M = rows; a.N = 3 * d; a.K = d; a.carry = m->carry;
+      a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
+      a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
+      a.pos = pos; a.n_tok = n_tok; a.d = d; a.hd = m->hd; a.H = c.n_heads;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
+      LD_TRY_HIP(launch_gemm_qkv(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_ATTN);
+      AttnArgs a{};
+      a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
+      a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
+      LD_TRY_HIP(launch_attention(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_WO);
+      GemmArgs a{};
+      a.A = att; a.W = m->layer(l, m->lay.o_wo); a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
+      a.resid = x;
+      LD_TRY_HIP(launch_gemm_resid(a, m->stream));
+    }
+    LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gffn), rows, d, 1, 0, c.norm_eps,
+                                   m->stream));
+    {
+      ProfScope ps(m, K_W13);
+      GemmArgs a{};
+      a.A = xn; a.W = m->layer(l, m->lay.o_w13); a.M = rows; a.N = 2 * f; a.K = d; a.carry = m->carry;
+      a.g_out = g; a.f = f;
+      LD_TRY_HIP(launch_gemm_swiglu(a, m->stream));
+    }
+    {
+      ProfScope ps(m, K_W2);
+      GemmArgs a{};
+      a.A = g; a.W = m->layer(l, m->lay.o_w2); a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
+      a.resid = x;
+      LD_TRY_HIP(launch_gemm_resid(a, m->stream));
+    }
+  }
+  return LD_OK;
+}
+
+// Final norm + classifier + arg-max for B sequences whose last rows sit at
+// x[b * n_tok + n_tok - 1] (all rows when all_pos).  Logits row of GEMM row r:
+// (r / n_tok) * out_rows_per_seq + out_row0 + r % n_tok.
+int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_rows_per_seq,
+         int out_row0, int* next) {
+  const ld_config& c = m->c;
+  const int d = c.dim, V = c.vocab_size;
+  float* x = m->at<float>(m->lay.x);
+  float* xn = m->at<float>(m->lay.xn);
+  float* pv = m->at<float>(m->lay.arg_val);
+  int* pi = m->at<int>(m->lay.arg_idx);
+  int* err = m->at<int>(m->lay.err);
+  int* next_int = m->at<int>(m->lay.next);
+  const int cls_rows = all_pos ? B * n_tok : B;
+  int nparts = 0;
+  // capacity of the partial arrays (R rows x the GEMM's 2 partials per 128 columns)
+  if (cls_rows > m->lay.rows) return LD_E_ARENA;
+  ProfScope ps(m, K_CLS);
+  if (cls_rows == 1) {
+    GemvArgs a{};
+    a.x = x + (size_t)(n_tok - 1) * d; a.gain = m->at<float>(m->lay.gain_final); a.eps = c.norm_eps;
+    a.W = m->at<float>(m->lay.Wcls); a.N = V; a.K = d;
+    a.logits = logits ? logits + (size_t)out_row0 * V : nullptr;
+    a.part_val = pv; a.part_idx = pi; a.err = err;
+    LD_TRY_HIP(launch_gemv_cls(a, &nparts, m->stream));
+  } else {
+    if (all_pos)
+      LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->at<float>(m->lay.gain_final), cls_rows, d, 1, 0,
+                                     c.norm_eps, m->stream));
+    else
+      LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->at<float>(m->lay.gain_final), B, d, n_tok, n_tok - 1,
+                                     c.norm_eps, m->stream));
+    GemmArgs a{};
+    a.A = xn; a.W = m->at<float>(m->lay.Wcls); a.M = cls_rows; a.N = V; a.K = d; a.carry = m->carry;
+    a.logits = logits;
+    a.n_tok = all_pos ? n_tok : 1;
+    a.logit_rows_per_seq = all_pos ? out_rows_per_seq : 1;
+    a.logit_row0 = all_pos ? out_row0 : 0;
+    a.part_val = pv; a.part_idx = pi; a.err = err;
+    LD_TRY_HIP(launch_gemm_cls(a, &nparts, m->stream));
+  }
+  // arg-max of each sequence's last row (every row is a last row unless all_pos)
+  const int stride = (all_pos && cls_rows > 1) ? n_tok : 1;
+  const int offset = (all_pos && cls_rows > 1) ? n_tok - 1 : 0;
+  LD_TRY_HIP(launch_argmax_finalize(pv, pi, B, nparts, stride, offset, next, next_int, m->stream));
+  return LD_OK;
+}
+
+bool tokens_valid(const int32_t* t, size_t n, int V) {
+  for (size_t i = 0; i < n; ++i)
+    if (t[i] < 0 || t[i] >= V) return false;
+  return true;
+}
+
+}  // namespace
+
+// ================================================================== C ABI ==
+
+extern "C" {
+
+int ld_arena_bytes(const ld_config* cfg, size_t* bytes_out) {
+  int rc = validate(cfg);
+  if (rc != LD_OK) return rc;
+  if (!bytes_out) return LD_E_INVAL;
+  Layout L;
+  make_layout(cfg, &L);
+  *bytes_out = L.total;
+  return LD_OK;
+}
+
+int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t arena_bytes,
+                  void* hip_stream, ld_model** out) {
+  int rc = validate(cfg);
+  if (rc != LD_OK) return rc;
+  if (!out || !dev_arena) return LD_E_INVAL;
+  Layout L;
+  make_layout(cfg, &L);
+  if ((reinterpret_cast<uintptr_t>(dev_arena) % kAlign) != 0 || arena_bytes < L.total)
+    return LD_E_ARENA;
+  ld_model* m = new (std::nothrow) ld_model();
+  if (!m) return LD_E_INVAL;
+  m->c = *cfg;
+  m->lay = L;
+  m->hd = cfg->dim / cfg->n_heads;
+  m->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  m->arena = reinterpret_cast<char*>(dev_arena);
+  m->pos = 0;
+  // fp32 MFMA sums are carried into fp64 for wide models (K >= 2048)
+  m->carry = cfg->dim >= 2048;
+  m->tok_slot = 0;
+  if (hipGetDevice(&m->device) != hipSuccess) {
+    delete m;
+    return LD_E_HIP;
+  }
+  for (int i = 0; i < kTokSlots; ++i) {
+    m->tok_host[i] = nullptr;
+    m->tok_ev_live[i] = false;
+  }
+  auto fail = [&](int code) {
+    ld_model_free(m);
+    return code;
+  };
+  for (int i = 0; i < kTokSlots; ++i) {
+    if (hipHostMalloc((void**)&m->tok_host[i], sizeof(int32_t) * L.rows, hipHostMallocDefault) !=
+            hipSuccess ||
+        hipEventCreateWithFlags(&m->tok_ev[i], hipEventDisableTiming) != hipSuccess)
+      return fail(LD_E_HIP);
+  }
+
+  const size_t d = cfg->dim, f = cfg->hidden_dim, V = cfg->vocab_size;
+  {
+    Uploader up;
+    up.s = m->stream;
+    up.seed = seed;
+    up.nthreads = host_threads();
+    up.cap = (size_t)16 << 20;   // 64 MiB per staging buffer
+    if (up.init() != LD_OK) return fail(LD_E_HIP);
+    up.plain(m->at<float>(L.E), synth_stream_embedding(), V * d);
+    for (int l = 0; l < cfg->n_layers && up.ok; ++l) {
+      float* wqkv = m->layer(l, L.o_wqkv);
+      up.plain(wqkv, synth_stream_layer(l, 0), d * d);
+      up.plain(wqkv + d * d, synth_stream_layer(l, 1), d * d);
+      up.plain(wqkv + 2 * d * d, synth_stream_layer(l, 2), d * d);
+      up.plain(m->layer(l, L.o_wo), synth_stream_layer(l, 3), d * d);
+      up.w13(m->layer(l, L.o_w13), synth_stream_layer(l, 4), synth_stream_layer(l, 6), f, d);
+      up.plain(m->layer(l, L.o_w2), synth_stream_layer(l, 5), d * f);
+      if (launch_fill(m->layer(l, L.o_gatt), 1.0f, d, m->stream) != hipSuccess ||
+          launch_fill(m->layer(l, L.o_gffn), 1.0f, d, m->stream) != hipSuccess)
+        up.ok = false;
+    }
+    if (up.ok && !cfg->tied_classifier)
+      up.plain(m->at<float>(L.Wcls), synth_stream_classifier(cfg->n_layers), V * d);
+    if (!up.ok) return fail(LD_E_HIP);
+    if (launch_fill(m->at<float>(L.gain_final), 1.0f, d, m->stream) != hipSuccess) return fail(LD_E_HIP);
+    // rotary tables: angle p * theta^(-2i/hd), cos/sin in double, stored fp32
+    const int half = m->hd / 2;
+    std::vector<float> ct((size_t)cfg->max_seq * half), st((size_t)cfg->max_seq * half);
+    for (int p = 0; p < cfg->max_seq; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double inv_freq = std::pow(cfg->rope_theta, -(2.0 * (double)i) / (double)m->hd);
+        const double ang = (double)p * inv_freq;
+        ct[(size_t)p * half + i] = (float)std::cos(ang);
+        st[(size_t)p * half + i] = (float)std::sin(ang);
+      }
+    if (hipMemcpyAsync(m->at<float>(L.rope_cos), ct.data(), ct.size() * 4, hipMemcpyHostToDevice,
+                       m->stream) != hipSuccess ||
+        hipMemcpyAsync(m->at<float>(L.rope_sin), st.data(), st.size() * 4, hipMemcpyHostToDevice,
+                       m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.Kc, 0, L.Vc - L.Kc, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.Vc, 0, L.x - L.Vc, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.err, 0, 4, m->stream) != hipSuccess ||
+        hipStreamSynchronize(m->stream) != hipSuccess)
+      return fail(LD_E_HIP);
+  }
+  *out = m;
+  return LD_OK;
+}
+
+int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
+                   float* dev_logits, int32_t* dev_next) {
+  if (!m || !tokens || batch <= 0 || batch > m->c.max_batch) return LD_E_INVAL;
+  if (m->pos + 1 > m->c.max_seq) return LD_E_RANGE;
+  if (!tokens_on_device && !tokens_valid(tokens, (size_t)batch, m->c.vocab_size)) return LD_E_INVAL;
+  DeviceGuard dg(m->device);
+  const int* d_tok = tokens_on_device ? tokens : m->at<int>(m->lay.tok);
+  if (!tokens_on_device) {
+    int rc = enqueue_host_tokens(m, tokens, (size_t)batch);
+    if (rc != LD_OK) return rc;
+  }
+  const ld_config& c = m->c;
+  LD_TRY_HIP(launch_embed(d_tok, m->at<float>(m->lay.E), m->at<float>(m->lay.x), batch, c.dim,
+                          c.vocab_size, m->at<int>(m->lay.err), m->stream));
+  int rc = (batch == 1) ? layers_gemv(m, m->pos) : layers_gemm(m, batch, 1, m->pos);
+  if (rc != LD_OK) return rc;
+  rc = head(m, batch, 1, false, dev_logits, 1, 0, dev_next);
+  if (rc != LD_OK) return rc;
+  m->pos += 1;
+  return LD_OK;
+}
+
+int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host_tokens,
+               float* dev_logits, int32_t* dev_next, int32_t all_pos) {
+  if (!m || !host_tokens || batch <= 0 || batch > m->c.max_batch || n_tokens <= 0) return LD_E_INVAL;
+  if ((int64_t)m->pos + n_tokens > m->c.max_seq) return LD_E_RANGE;
+  if (!tokens_valid(host_tokens, (size_t)batch * n_tokens, m->c.vocab_size)) return LD_E_INVAL;
+  DeviceGuard dg(m->device);
+  const ld_config& c = m->c;
+  const int R = m->lay.rows;
+  const int nc_max = std::max(1, R / batch);   // positions per chunk
+  std::vector<int32_t> chunk_tok;
+  const int pos0 = m->pos;
+  for (int t0 = 0; t0 < n_tokens; t0 += nc_max) {
+    const int nc = std::min(nc_max, n_tokens - t0);
+    const int rows = batch * nc;
+    chunk_tok.resize((size_t)rows);
+    for (int b = 0; b < batch; ++b)
+      std::memcpy(&chunk_tok[(size_t)b * nc], host_tokens + (size_t)b * n_tokens + t0,
+                  sizeof(int32_t) * nc);
+    int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows);
+    if (rc != LD_OK) return rc;
+    LD_TRY_HIP(launch_embed(m->at<int>(m->lay.tok), m->at<float>(m->lay.E), m->at<float>(m->lay.x),
+                            rows, c.dim, c.vocab_size, m->at<int>(m->lay.err), m->stream));
+    rc = (rows == 1) ? layers_gemv(m, pos0 + t0) : layers_gemm(m, rows, nc, pos0 + t0);
+    if (rc != LD_OK) return rc;
+    const bool last = t0 + nc >= n_tokens;
+    if (all_pos || last) {
+      rc = head(m, batch, nc, all_pos != 0, dev_logits, n_tokens, all_pos ? t0 : 0,
+                last ? dev_next : nullptr);
+      if (rc != LD_OK) return rc;
+    }
+  }
+  m->pos = pos0 + n_tokens;
+  return LD_OK;
+}
+
+int ld_kv_reset(ld_model* m) {
+  if (!m) return LD_E_INVAL;
+  m->pos = 0;
+  return LD_OK;
+}
+
+int ld_set_pos(ld_model* m, int32_t new_pos) {
+  if (!m) return LD_E_INVAL;
+  if (new_pos < 0 || new_pos > m->pos) return LD_E_RANGE;
+  m->pos = new_pos;
+  return LD_OK;
+}
+
+int ld_get_pos(const ld_model* m, int32_t* pos) {
+  if (!m || !pos) return LD_E_INVAL;
+  *pos = m->pos;
+  return LD_OK;
+}
+
+int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, float* host_out) {
+  if (!m || !host_out) return LD_E_INVAL;
+  const ld_config& c = m->c;
+  const uint64_t d = c.dim, f = c.hidden_dim, V = c.vocab_size, NL = c.n_layers;
+  DeviceGuard dg(m->device);
+  const float* base = nullptr;
+  uint64_t total = 0;
+  int kind = -1, layer = -1;
+  if (stream_id == 0) {
+    base = m->at<float>(m->lay.E);
+    total = V * d;
+  } else if (stream_id == (int64_t)(1 + 7 * NL)) {
+    if (c.tied_classifier) return LD_E_INVAL;
+    base = m->at<float>(m->lay.Wcls);
+    total = V * d;
+  } else if (stream_id >= 1 && stream_id <= (int64_t)(7 * NL)) {
+    layer = (int)((stream_id - 1) / 7);
+    kind = (int)((stream_id - 1) % 7);
+    switch (kind) {
+      case 0: base = m->layer(layer, m->lay.o_wqkv); total = d * d; break;
+      case 1: base = m->layer(layer, m->lay.o_wqkv) + d * d; total = d * d; break;
+      case 2: base = m->layer(layer, m->lay.o_wqkv) + 2 * d * d; total = d * d; break;
+      case 3: base = m->layer(layer, m->lay.o_wo); total = d * d; break;
+      case 5: base = m->layer(layer, m->lay.o_w2); total = d * f; break;
+      default: base = m->layer(layer, m->lay.o_w13); total = f * d; break;   // W1 (4), W3 (6)
+    }
+  } else {
+    return LD_E_INVAL;
+  }
+  if (start > total || n > total - start) return LD_E_RANGE;
+  if (kind == 4 || kind == 6) {
+    // interleaved 32-row blocks: copy row pieces
+    uint64_t i = start;
+    while (i < start + n) {
+      const uint64_t r = i / d, col = i % d;
+      const uint64_t dev_row = (r / 32) * 64 + (r % 32) + (kind == 6 ? 32 : 0);
+      const uint64_t cnt = std::min(d - col, start + n - i);
+      LD_TRY_HIP(hipMemcpyAsync(host_out + (i - start), base + dev_row * d + col, cnt * 4,
+                                hipMemcpyDeviceToHost, m->stream));
+      i += cnt;
+    }
+  } else {
+    LD_TRY_HIP(hipMemcpyAsync(host_out, base + start, n * 4, hipMemcpyDeviceToHost, m->stream));
+  }
+  LD_TRY_HIP(hipStreamSynchronize(m->stream));
+  return LD_OK;
+}
+
+int ld_status(ld_model* m) {
+  if (!m) return LD_E_INVAL;
+  DeviceGuard dg(m->device);
+  int err = 0;
+  LD_TRY_HIP(hipMemcpyAsync(&err, m->at<int>(m->lay.err), 4, hipMemcpyDeviceToHost, m->stream));
+  LD_TRY_HIP(hipStreamSynchronize(m->stream));
+  if (err != 0) {
+    LD_TRY_HIP(hipMemsetAsync(m->at<int>(m->lay.err), 0, 4, m->stream));
+    LD_TRY_HIP(hipStreamSynchronize(m->stream));
+    return LD_E_NONFINITE;
+  }
+  return LD_OK;
+}
+
+int ld_profile(ld_model* m, int32_t kernel_class, int32_t enable) {
+  if (!m || kernel_class < 0 || kernel_class >= LD_K_COUNT) return LD_E_INVAL;
+  DeviceGuard dg(m->device);
+  Prof& p = m->prof[kernel_class];
+  if (enable && p.ev.empty()) {
+    p.ev.resize(2 * kProfPairs);
+    for (auto& e : p.ev) LD_TRY_HIP(hipEventCreate(&e));
+  }
+  p.on = enable != 0;
+  p.used = 0;
+  return LD_OK;
+}
+
+int ld_profile_read(ld_model* m, int32_t kernel_class, double* avg_ms, int64_t* count) {
+  if (!m || !avg_ms || !count || kernel_class < 0 || kernel_class >= LD_K_COUNT) return LD_E_INVAL;
+  DeviceGuard dg(m->device);
+  Prof& p = m->prof[kernel_class];
+  LD_TRY_HIP(hipStreamSynchronize(m->stream));
+  double sum = 0.0;
+  for (int i = 0; i < p.used; ++i) {
+    float ms = 0.f;
+    LD_TRY_HIP(hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]));
+    sum += ms;
+  }
+  *count = p.used;
+  *avg_ms = p.used ? sum / p.used : 0.0;
+  p.used = 0;
+  return LD_OK;
+}
+
+int ld_synth_prompt(uint64_t seed, uint64_t seq, int32_t n, int32_t lo, int32_t hi, int32_t* host_out) {
+  if (!host_out || n < 0 || hi <= lo) return LD_E_INVAL;
+  synth_prompt(host_out, seed, seq, (size_t)n, lo, hi);
+  return LD_OK;
+}
+
+void ld_model_free(ld_model* m) {
+  if (!m) return;
+  DeviceGuard dg(m->device);
+  hipStreamSynchronize(m->stream);
+  for (int i = 0; i < kTokSlots; ++i) {
+    if (m->tok_host[i]) {
+      hipHostFree(m->tok_host[i]);
+      hipEventDestroy(m->tok_ev[i]);
+    }
+  }
+  for (auto& p : m->prof)
+    for (auto& e : p.ev) hipEventDestroy(e);
+  delete m;
+}
+
+const char* ld_strerror(int code) {
+  switch (code) {
+    case LD_OK: return "ok";
+    case LD_E_INVAL: return "invalid argument";
+    case LD_E_RANGE: return "position out of range (max_seq reached)";
+    case LD_E_ARENA: return "arena too small or misaligned";
+    case LD_E_HIP: return "HIP runtime error";
+    case LD_E_NONFINITE: return "non-finite logit or out-of-range device token";
+    case LD_E_STATE: return "invalid state";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

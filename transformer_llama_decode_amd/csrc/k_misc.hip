@@ -1,0 +1,120 @@
+// k_misc.hip -- small kernels around the projections: token embedding gather,
+// row-wise RMSNorm for the GEMM path, the final arg-max over classifier partials.
+#include "dev_common.hpp"
+#include "ld_internal.hpp"
+
+namespace ld {
+
+namespace {
+
+// x[r] = E[tok[r]]; an out-of-range id (only possible for ids read from device
+// memory) is replaced by 0 and flagged.
+__global__ void __launch_bounds__(256) k_embed(const int* tok, const float* E, float* x, int d, int V,
+                                               int* err) {
+  const int r = blockIdx.x;
+  int t = tok[r];
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 2);
+    t = 0;
+  }
+  const float4* src = reinterpret_cast<const float4*>(E + (size_t)t * d);
+  float4* dst = reinterpret_cast<float4*>(x + (size_t)r * d);
+  for (int j = threadIdx.x; j < (d >> 2); j += 256) dst[j] = src[j];
+}
+
+// out[i] = RMSNorm(in[i * in_stride + in_offset]) * gain, rounded to fp32.
+__global__ void __launch_bounds__(256) k_rmsnorm_rows(const float* in, float* out, const float* gain,
+                                                      int d, int in_stride, int in_offset,
+                                                      double eps) {
+  __shared__ double red[4];
+  const int i = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float4* x4 = reinterpret_cast<const float4*>(in + ((size_t)i * in_stride + in_offset) * d);
+  float4* y4 = reinterpret_cast<float4*>(out + (size_t)i * d);
+  const float4* g4 = reinterpret_cast<const float4*>(gain);
+  double ss = 0.0;
+  for (int j = threadIdx.x; j < (d >> 2); j += 256) {
+    const float4 v = x4[j];
+    ss = fma((double)v.x, (double)v.x, ss);
+    ss = fma((double)v.y, (double)v.y, ss);
+    ss = fma((double)v.z, (double)v.z, ss);
+    ss = fma((double)v.w, (double)v.w, ss);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  const double inv = 1.0 / sqrt((((red[0] + red[1]) + red[2]) + red[3]) / (double)d + eps);
+  for (int j = threadIdx.x; j < (d >> 2); j += 256) {
+    float4 v = x4[j];
+    const float4 g = g4[j];
+    v.x = (float)((double)v.x * inv * (double)g.x);
+    v.y = (float)((double)v.y * inv * (double)g.y);
+    v.z = (float)((double)v.z * inv * (double)g.z);
+    v.w = (float)((double)v.w * inv * (double)g.w);
+    y4[j] = v;
+  }
+}
+
+// next[r] = index of the best (value, index) among the row's partials.
+// Output row r reads partial row r * row_stride + row_offset.
+__global__ void __launch_bounds__(256) k_argmax_finalize(const float* pv, const int* pi, int nparts,
+                                                         int row_stride, int row_offset, int* next,
+                                                         int* next2) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const size_t src = ((size_t)r * row_stride + row_offset) * nparts;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int p = threadIdx.x; p < nparts; p += 256) argmax_merge(bv, bi, pv[src + p], pi[src + p]);
+  wave_argmax(bv, bi, 64);
+  if (lane == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k) argmax_merge(bv, bi, sv[k], si[k]);
+    if (bi == 0x7fffffff) bi = 0;   // every value was NaN: flagged by the producer
+    if (next) next[r] = bi;
+    if (next2) next2[r] = bi;
+  }
+}
+
+__global__ void k_fill(float* p, float v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_embed(const int* tok, const float* E, float* x, int rows, int d, int V, int* err,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(const float* in, float* out, const float* gain, int rows, int d,
+                               int in_stride, int in_offset, double eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(rows), dim3(256), 0, s, in, out, gain, d, in_stride,
+                     in_offset, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finalize(const float* part_val, const int* part_idx, int rows, int nparts,
+                                  int row_stride, int row_offset, int* next, int* next2,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(rows), dim3(256), 0, s, part_val, part_idx, nparts,
+                     row_stride, row_offset, next, next2);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, float v, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace ld

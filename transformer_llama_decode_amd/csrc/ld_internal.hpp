@@ -1,0 +1,130 @@
+// ld_internal.hpp -- device-side layout and kernel launchers of the decode library.
+//
+// HBM layout (one caller-owned arena, every region 256-byte aligned):
+//   E      [V][d]                 token embedding (also the classifier when tied)
+//   per layer l:
+//     Wqkv [3d][d]                Wq rows, then Wk rows, then Wv rows
+//     Wo   [d][d]
+//     W13  [2f][d]                W1 and W3 interleaved in 32-row blocks:
+//                                 rows 64j..64j+31 = W1 rows 32j..32j+31,
+//                                 rows 64j+32..64j+63 = W3 rows 32j..32j+31
+//     W2   [d][f]
+//     gain_att [d], gain_ffn [d]
+//   Wcls   [V][d]                 only when untied
+//   gain_final [d]
+//   rope_cos, rope_sin [S][hd/2]  fp32, from double on the host
+//   K cache [L][Bmax][H][Sp/64][hd][64]  (Sp = S rounded up to 64): each 64-position
+//                                 tile stored dimension-major, so a wave reading one
+//                                 dimension of 64 consecutive positions is coalesced
+//   V cache [L][Bmax][H][Sp][hd]  position-major rows
+//   activations for up to R rows: x, xn, q, att [R][d]; g [R][f]
+//   attention partials, arg-max partials, token buffers, error flag
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/ld.h"
+
+namespace ld {
+
+constexpr int kAlign = 256;
+constexpr int kMaxAttnParts = 1024;   // (row, head, chunk) partials when a head is split
+
+enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS = 5 };
+
+struct Layout {
+  size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
+  size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
+  size_t x, xn, q, att, g, attn_part, arg_val, arg_idx, tok, next, err;
+  size_t total;
+  int rows;            // R: activation rows per forward pass
+  int seq_pad;         // Sp
+  size_t arg_parts;    // capacity of the arg-max partial arrays
+};
+
+// ---- kernel launchers (return hipError_t of the launch) ----
+struct GemvArgs {
+  const float* x;      // input vector [K]
+  const float* gain;   // RMSNorm gain [K], or nullptr: no normalisation
+  double eps;
+  const float* W;      // rows of K floats
+  int N, K;
+  // QKV epilogue
+  float* q_out;
+  float* kc;           // K cache of (layer, sequence 0)
+  float* vc;           // V cache of (layer, sequence 0)
+  const float* rcos;
+  const float* rsin;
+  int pos, d, hd, seq_pad;
+  // residual epilogue
+  float* resid;
+  // SwiGLU epilogue
+  float* g_out;
+  // classifier epilogue
+  float* logits;       // may be nullptr
+  float* part_val;
+  int* part_idx;
+  int* err;
+};
+
+hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_resid(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s);
+// returns the number of arg-max partials written in *nparts
+hipError_t launch_gemv_cls(const GemvArgs& a, int* nparts, hipStream_t s);
+
+struct AttnArgs {
+  const float* q;      // [rows][d], rotated
+  const float* kc;     // K cache of this layer, sequence 0
+  const float* vc;     // V cache of this layer, sequence 0
+  float* out;          // [rows][d]
+  double* part;        // partial (o[hd], m, l) per (row, head, chunk)
+  int rows, n_tok, pos, d, H, hd, seq_pad, bmax;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+struct GemmArgs {
+  const float* A;      // [M][K]
+  const float* W;      // [N][K]
+  int M, N, K;
+  bool carry;          // fp32 MFMA partial sums carried into fp64 every 32 k
+  // QKV epilogue
+  float* q_out;
+  float* kc;
+  float* vc;
+  const float* rcos;
+  const float* rsin;
+  int pos, n_tok, d, hd, H, seq_pad, bmax;
+  // residual
+  float* resid;
+  // SwiGLU
+  float* g_out;
+  int f;
+  // classifier
+  float* logits;       // may be nullptr
+  int logit_rows_per_seq;   // output row of GEMM row m: (m / n_tok) * logit_rows_per_seq + logit_row0 + m % n_tok
+  int logit_row0;
+  float* part_val;
+  int* part_idx;
+  int* err;
+};
+hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_cls(const GemmArgs& a, int* nparts, hipStream_t s);
+
+hipError_t launch_embed(const int* tok, const float* E, float* x, int rows, int d, int V, int* err,
+                        hipStream_t s);
+// out row i <- rmsnorm(in row i * in_stride + in_offset)
+hipError_t launch_rmsnorm_rows(const float* in, float* out, const float* gain, int rows, int d,
+                               int in_stride, int in_offset, double eps, hipStream_t s);
+// next[r] (and next2[r]) = arg-max of partial row r * row_stride + row_offset
+hipError_t launch_argmax_finalize(const float* part_val, const int* part_idx, int rows, int nparts,
+                                  int row_stride, int row_offset, int* next, int* next2,
+                                  hipStream_t s);
+hipError_t launch_fill(float* p, float v, size_t n, hipStream_t s);
+
+}  // namespace ld

@@ -1,0 +1,259 @@
+"""Decode throughput of the fp32 Llama-2-architecture path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5]
+
+One step = one decode position of the whole forward pass (embedding, every
+layer's RMSNorm, Q/K/V + rotary + KV write, attention over the cache, Wo +
+residual, RMSNorm, SwiGLU FFN + residual, final norm, classifier, greedy
+arg-max), tokens fed back on the device.  Default workload: the 7B shape at
+batch 1 (512-token random prompt prefilled, then decode positions 512..1023),
+weights N(0, 0.02) from seed 4, all resident in HBM before timing starts.
+
+Prints one JSON line with the throughput, the dominant kernel's roofline
+(measured with HIP events on the library's stream inside the timed region) and
+the CPU oracle timed on this host on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/sec at batch 1 (15M/44M/7B-shape fp32) + achieved HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+W13_SOURCES = ["transformer_llama_decode_amd/csrc/k_gemv.hip", "transformer_llama_decode_amd/csrc/dev_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w13_gemv_7b.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(cfg, pos, batch=1):
+    """Algorithmic HBM bytes of one decode step at position pos: every matrix
+    once, plus per sequence the embedding row, norm gains, the K/V history read
+    (positions 0..pos), the new K/V written and the logits written."""
+    d, f, V, L = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers
+    weights = 4 * (L * (4 * d * d + 3 * d * f) + V * d)
+    gains = 4 * (2 * L + 1) * d
+    per_seq = 4 * (d + 2 * L * (pos + 1) * d + 2 * L * d + V)
+    return weights + gains + batch * per_seq
+
+
+def w13_launch_bytes(cfg):
+    """Algorithmic bytes of one W1/W3 + SwiGLU launch at batch 1: both weight
+    matrices once, the input row and its gain read, the gate row written."""
+    d, f = cfg.dim, cfg.hidden_dim
+    return 4 * (2 * f * d + 2 * d + f)
+
+
+def sources_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per W13 launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != sources_hash(W13_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, n_steps):
+    """The oracle (plain single-threaded C, fp64 accumulation) on this host."""
+    import numpy as np
+    from oracle import oracle as O
+    t0 = time.time()
+    m = O.OracleModel(w.model, w.model_seed, nthreads=min(16, os.cpu_count() or 1))
+    gen_s = time.time() - t0
+    st = m.new_state()
+    logits = np.empty(w.model.vocab_size, np.float32)
+    tok = 1
+    t0 = time.perf_counter()
+    for p in range(n_steps):
+        tok, _ = m.forward(st, tok, p, logits)
+    dt = time.perf_counter() - t0
+    m.close()
+    return {
+        "value": n_steps / dt, "unit": "tok/s", "cores": 1, "kind": "oracle",
+        "sample": "%d decode positions (p=0..%d) of the %s model, batch 1, one host thread, "
+                  "gcc -O3, fp32 storage / fp64 accumulation; weights drawn beforehand in %.0fs"
+                  % (n_steps, n_steps - 1, w.name, gen_s),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="C5")
+    ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the decode path on a single "
+              "MI355X (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 29   # 2 GiB of fp32
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n,
+                          "launches": 6, "copy_ms": round(dt * 1e3, 3),
+                          "copy_gbps_read_plus_write": round(8 * n / dt / 1e9, 1)}))
+        return
+
+    from transformer_llama_decode_amd.configs import WORKLOADS
+    from transformer_llama_decode_amd.model import LlamaDecoder, synth_prompt
+    from transformer_llama_decode_amd._lib import LD_K_W13
+
+    w = WORKLOADS[args.workload]
+    cfg = w.model
+    B = 1
+    P = max(w.prompt_len, 1)
+    if P + max(args.steps, args.warmup) > cfg.max_seq:
+        sys.exit("steps + prompt exceed max_seq %d" % cfg.max_seq)
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    gm = LlamaDecoder(cfg, w.model_seed)
+    torch.cuda.synchronize()
+    log("init %.1fs (%s, arena %.2f GB)" % (time.time() - t0, w.name, gm.arena.numel() / 1e9))
+
+    prompt = synth_prompt(w.prompt_seed, 0, w.prompt_len) if w.prompt_len else np.array([w.start_token], np.int32)
+    bufs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    # prefill (timed on its own)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if w.prompt_len:
+        gm.prefill(prompt[None, :], next_out=bufs[0])
+    else:
+        gm.decode_step(prompt, next_out=bufs[0])
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    log("prefill %d tokens: %.1f ms" % (len(prompt), prefill_s * 1e3))
+
+    def run(k, tok):
+        for i in range(k):
+            out = bufs[(i + 1) % 2] if tok is bufs[i % 2] else bufs[i % 2]
+            gm.decode_step(tok, next_out=out)
+            tok = out
+        return tok
+
+    tok = run(args.warmup, bufs[0])
+    torch.cuda.synchronize()
+    gm.set_pos(P)                      # time exactly the workload's positions P .. P+steps-1
+    start_tok = tok
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    run(args.steps, start_tok)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    # The dominant kernel, timed with HIP events recorded around each of its
+    # launches on the library's stream, over the same positions again (event
+    # records stall the stream for a few microseconds, so they stay out of the
+    # pass that gives the throughput).
+    gm.set_pos(P)
+    gm.profile(LD_K_W13, True)
+    run(args.steps, start_tok)
+    w13_ms, w13_n = gm.profile_read(LD_K_W13)
+    gm.profile(LD_K_W13, False)
+    status = gm.status()
+    if status != 0:
+        sys.exit("device reported error %d during the run" % status)
+
+    elapsed = wall
+    tok_s = B * args.steps / elapsed
+    avg_bytes = sum(step_bytes(cfg, p, B) for p in range(P, P + args.steps)) / args.steps
+    w13_bytes = w13_launch_bytes(cfg)
+    achieved = w13_bytes / (w13_ms * 1e-3) / 1e9 if w13_ms > 0 else None
+    traffic = measured_traffic()
+    log("decode: %.2f ms/step, %.1f tok/s, %.0f GB/s over the step; W13 %.3f ms x %d -> %.0f GB/s"
+        % (elapsed / args.steps * 1e3, tok_s, avg_bytes * tok_s / 1e9, w13_ms, w13_n, achieved or 0))
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tok_s, 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s" % (w.name, w.description),
+            "batch": B,
+            "positions": "%d..%d" % (P, P + args.steps - 1),
+            "prompt_tokens": int(len(prompt)),
+            "seed": w.model_seed,
+        },
+        "hbm_gbps_step": round(avg_bytes * tok_s / 1e9, 1),
+        "hbm_frac_step": round(avg_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": int(avg_bytes),
+        "gpu_event_ms_per_step": round(gpu_s / args.steps * 1e3, 4),
+        "prefill_ms": round(prefill_s * 1e3, 2),
+        "prefill_tok_s": round(len(prompt) / prefill_s, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "W1/W3 + SwiGLU GEMV (k_gemv<EPI_SWIGLU>), batch 1",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+            "traffic": traffic,
+            "bytes_per_launch": w13_bytes,
+            "avg_launch_ms": round(w13_ms, 5),
+            "launches": w13_n,
+            "timing": "HIP event pairs on the library's stream around every launch, in a "
+                      "second pass over the timed positions",
+        },
+    }
+    gm.close()
+    del gm
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline: drawing weights for the oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -64,9 +64,12 @@ __device__ __forceinline__ void rope_pair(float y0, float y1, float c, float s, 
   o1 = (float)(a * ss + b * cc);
 }
 
-// Index of element (position p, dimension i) in a head's K-cache tiles [Sp/64][hd][64].
+// Index of element (position p, dimension i) in a head's K-cache tiles
+// [Sp/64][hd/4][64][4]: within a 64-position tile, 4 consecutive dimensions of
+// one position are one float4, and lane j of a wave reading float4 column i/4
+// of the tile gets position j -- 1 KiB contiguous per wave load.
 __device__ __forceinline__ size_t ktile_index(int p, int i, int hd) {
-  return ((size_t)(p >> 6) * hd + i) * 64 + (p & 63);
+  return (((size_t)(p >> 6) * (hd >> 2) + (i >> 2)) * 64 + (p & 63)) * 4 + (i & 3);
 }
 
 }  // namespace ld

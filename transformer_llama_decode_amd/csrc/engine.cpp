@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kMaxRowsCap = 4096;     // activation rows per forward pass (prefill is chunked)
 constexpr int kTokSlots = 4;          // pinned host slots for host token ids
-constexpr int kProfPairs = 8192;      // event pairs per profiled kernel class
+constexpr int kProfPairs = 1 << 15;   // event pairs per profiled kernel class
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -79,6 +79,7 @@ void make_layout(const ld_config* c, Layout* L) {
   L->att = take(R * d * 4);
   L->g = take(R * f * 4);
   L->attn_part = take((size_t)kMaxAttnParts * (hd + 2) * 8);
+  L->attn_ticket = take((size_t)kMaxAttnParts * 4);
   L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
   L->arg_val = take(L->arg_parts * 4);
   L->arg_idx = take(L->arg_parts * 4);
@@ -104,6 +105,7 @@ struct ld_model {
   char* arena;
   int pos;
   bool carry;
+  bool stream_weights;   // weights exceed the Infinity Cache: stream them non-temporally
   int* tok_host[kTokSlots];
   hipEvent_t tok_ev[kTokSlots];
   bool tok_ev_live[kTokSlots];
@@ -293,7 +295,7 @@ int layers_gemv(ld_model* m, int pos) {
       ProfScope ps(m, K_QKV);
       GemvArgs a{};
       a.x = x; a.gain = m->layer(l, m->lay.o_gatt); a.eps = c.norm_eps;
-      a.W = m->layer(l, m->lay.o_wqkv); a.N = 3 * d; a.K = d;
+      a.W = m->layer(l, m->lay.o_wqkv); a.N = 3 * d; a.K = d; a.stream = m->stream_weights;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
       a.pos = pos; a.d = d; a.hd = m->hd; a.seq_pad = m->lay.seq_pad;
@@ -303,6 +305,7 @@ int layers_gemv(ld_model* m, int pos) {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
+      a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
       LD_TRY_HIP(launch_attention(a, m->stream));
@@ -311,6 +314,7 @@ int layers_gemv(ld_model* m, int pos) {
       ProfScope ps(m, K_WO);
       GemvArgs a{};
       a.x = att; a.W = m->layer(l, m->lay.o_wo); a.N = d; a.K = d; a.resid = x;
+      a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_resid(a, m->stream));
     }
     {
@@ -318,12 +322,14 @@ int layers_gemv(ld_model* m, int pos) {
       GemvArgs a{};
       a.x = x; a.gain = m->layer(l, m->lay.o_gffn); a.eps = c.norm_eps;
       a.W = m->layer(l, m->lay.o_w13); a.N = f; a.K = d; a.g_out = g;
+      a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_swiglu(a, m->stream));
     }
     {
       ProfScope ps(m, K_W2);
       GemvArgs a{};
       a.x = g; a.W = m->layer(l, m->lay.o_w2); a.N = d; a.K = f; a.resid = x;
+      a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_resid(a, m->stream));
     }
   }
@@ -356,6 +362,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
+      a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
       LD_TRY_HIP(launch_attention(a, m->stream));
@@ -408,7 +415,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
   if (cls_rows == 1) {
     GemvArgs a{};
     a.x = x + (size_t)(n_tok - 1) * d; a.gain = m->at<float>(m->lay.gain_final); a.eps = c.norm_eps;
-    a.W = m->at<float>(m->lay.Wcls); a.N = V; a.K = d;
+    a.W = m->at<float>(m->lay.Wcls); a.N = V; a.K = d; a.stream = m->stream_weights;
     a.logits = logits ? logits + (size_t)out_row0 * V : nullptr;
     a.part_val = pv; a.part_idx = pi; a.err = err;
     LD_TRY_HIP(launch_gemv_cls(a, &nparts, m->stream));
@@ -476,6 +483,12 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
   m->pos = 0;
   // fp32 MFMA sums are carried into fp64 for wide models (K >= 2048)
   m->carry = cfg->dim >= 2048;
+  {
+    const size_t wbytes = 4 * ((size_t)cfg->n_layers * (4 * (size_t)cfg->dim * cfg->dim +
+                                                          3 * (size_t)cfg->dim * cfg->hidden_dim) +
+                               (size_t)cfg->vocab_size * cfg->dim * (cfg->tied_classifier ? 1 : 2));
+    m->stream_weights = wbytes > ((size_t)256 << 20);
+  }
   m->tok_slot = 0;
   if (hipGetDevice(&m->device) != hipSuccess) {
     delete m;
@@ -538,6 +551,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
         hipMemsetAsync(m->arena + L.Kc, 0, L.Vc - L.Kc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.Vc, 0, L.x - L.Vc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.err, 0, 4, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.attn_ticket, 0, (size_t)kMaxAttnParts * 4, m->stream) != hipSuccess ||
         hipStreamSynchronize(m->stream) != hipSuccess)
       return fail(LD_E_HIP);
   }

@@ -1,22 +1,23 @@
 // k_attn.hip -- causal attention of query rows over the KV cache.
 //
-// One workgroup (4 waves) takes one (row, head, chunk of positions).  The chunk
-// is walked in tiles of 64 positions, one position per lane:
-//  * scores: wave w computes the partial dot over head dimensions
-//    [w*hd/4, (w+1)*hd/4) for the 64 positions of the tile.  K-cache tiles are
-//    stored dimension-major ([hd][64] per tile), so each load instruction reads
-//    64 consecutive positions of one dimension: 256 contiguous bytes.  The four
-//    partials meet in LDS and are summed in a fixed order;
-//  * an online softmax (running max m, running sum l, rescaled output) is kept
-//    per wave with wave-level max/sum butterflies -- every wave computes the
-//    same m and l from the same scores, so no second barrier is needed;
-//  * weighted values: wave w takes 16 of the tile's positions; lanes own head
-//    dimensions and read V rows (position-major) coalesced;
+// One workgroup (4 waves) takes one (row, head, chunk of 64-position tiles).
+// For each tile all four waves first issue every load of the tile at once --
+// wave w fetches head dimensions [w*hd/4, (w+1)*hd/4) of the tile's 64 keys
+// (K tiles are [hd/4][64][4], so each load is a float4 per lane, 1 KiB per
+// wave) and the 16 value rows of positions [16w, 16w+16) -- so a tile costs
+// about one HBM round trip.  Then:
+//  * scores: each wave's partial dot products over its dimensions meet in LDS
+//    and are summed in a fixed order (lane j = position j of the tile);
+//  * online softmax per wave with wave-level max/sum butterflies: every wave
+//    derives the same running max m and sum l from the same scores;
+//  * weighted values: wave w accumulates its 16 positions; lanes own head
+//    dimensions; the four partial outputs are summed in LDS at the end;
 //  * all arithmetic after the fp32 loads is fp64 (scores, exp, sums, weighted
 //    sum), rounded once when the output is stored.
-// A head whose history is long is split over several chunks (flash-decoding
-// style) so that one token's attention fills the GPU; the per-chunk (o, m, l)
-// partials are merged in a second, fixed-order kernel.
+// When few (row, head) pairs exist (batch-1 decode) each tile gets its own
+// workgroup so one token's attention is spread over the GPU (flash-decoding
+// style); the per-tile (o, m, l) partials are merged by the last workgroup of
+// each (row, head) to finish, found with an atomic ticket -- no second launch.
 #include "dev_common.hpp"
 #include "ld_internal.hpp"
 
@@ -27,66 +28,158 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 constexpr int kMaxHd = 256;
+constexpr int kSplitBelow = 512;   // split heads over tiles when rows*heads is below this
+constexpr bool kFusedMerge = false;   // measured: agent-scope fences cost more than a merge launch
 
-template <int DPL>
-__global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int chunk) {
-  __shared__ double qs[kMaxHd];
+// Merge the chunk partials (o_c, m_c, l_c) of one (row, head) into the output:
+// o = sum_c o_c e^(m_c - m) / sum_c l_c e^(m_c - m), m = max_c m_c.  One workgroup.
+__device__ void merge_unit(const AttnArgs& a, int r, int h, int nchunk) {
+  __shared__ double wc[kMaxAttnParts];
+  __shared__ double l_tot;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hd = a.hd;
+  const double* pu = a.part + ((size_t)r * a.H + h) * nchunk * (hd + 2);
+  if (w == 0) {
+    double m = -INFINITY;
+    for (int cc = lane; cc < nchunk; cc += kWave) m = fmax(m, pu[(size_t)cc * (hd + 2) + hd]);
+    m = wave_max(m);
+    double l = 0.0;
+    for (int cc = lane; cc < nchunk; cc += kWave) {
+      const double* pc = pu + (size_t)cc * (hd + 2);
+      const double wgt = pc[hd + 1] > 0.0 ? exp(pc[hd] - m) : 0.0;   // empty chunks weigh 0
+      wc[cc] = wgt;
+      l = fma(pc[hd + 1], wgt, l);
+    }
+    l = wave_sum(l);
+    if (lane == 0) l_tot = l;
+  }
+  __syncthreads();
+  float* out = a.out + (size_t)r * a.d + (size_t)h * hd;
+  for (int i = threadIdx.x; i < hd; i += kThreads) {
+    double acc = 0.0;
+    for (int cc = 0; cc < nchunk; ++cc)
+      if (wc[cc] != 0.0) acc = fma(pu[(size_t)cc * (hd + 2) + i], wc[cc], acc);
+    out[i] = (float)(acc / l_tot);
+  }
+}
+
+// K and V of one 64-position tile as one wave loads them: head dimensions
+// [w*HD/4, (w+1)*HD/4) of the 64 keys, and the value rows of positions [16w, 16w+16)
+// (lane l holds dimensions l*DPL .. l*DPL+DPL-1 of each row).
+template <int HD>
+struct TileRegs {
+  static constexpr int KQ = HD / 16, DPL = (HD + 63) / 64;
+  float4 k[KQ];
+  float v[16][DPL];
+};
+
+template <int HD>
+__device__ __forceinline__ void load_tile(TileRegs<HD>& t, const float4* kt, const float* vb, int tile,
+                                          int kvlen, int w, int lane) {
+  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
+  const int j0 = tile * kTile;
+  const float4* kp = kt + ((size_t)tile * (HD / 4) + w * KQ) * kTile + lane;
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) t.k[i] = kp[i * kTile];
+  const int vrows = kvlen - (j0 + 16 * w);   // rows of this wave inside the history (may be <= 0)
+  const float* vp = vb + (size_t)(j0 + 16 * w) * HD + lane * DPL;
+  const bool lane_in = lane * DPL < HD;
+  if (vrows >= 16 && lane_in) {              // the common case: the whole slice is history
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      if (DPL == 2) {
+        const float2 v2 = *reinterpret_cast<const float2*>(vp + jj * HD);
+        t.v[jj][0] = v2.x;
+        t.v[jj][DPL - 1] = v2.y;
+      } else {
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) t.v[jj][k] = vp[jj * HD + k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) t.v[jj][k] = (jj < vrows && lane_in) ? vp[jj * HD + k] : 0.f;
+  }
+}
+
+template <int HD, bool FUSED>   // HD: head dimension (a multiple of 16, <= 256); FUSED: the
+// last chunk to finish merges (atomic ticket), else a separate merge launch
+__global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int tiles_per_chunk) {
+  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
+  constexpr int hd = HD;
+  __shared__ float4 qs4[kMaxHd / 4];
   __shared__ double sp[4][kTile];
+  __shared__ double es[kTile];
   __shared__ double ow[4][kMaxHd];
+  __shared__ int is_last;
   const int c = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int hd = a.hd;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = r / a.n_tok, t = r - b * a.n_tok;
   const int kvlen = a.pos + t + 1;
-  const int start = c * chunk;
-  const int end = min(start + chunk, kvlen);
+  const int ntiles = (kvlen + kTile - 1) / kTile;
+  const int tile0 = c * tiles_per_chunk;
+  const int tile1 = min(tile0 + tiles_per_chunk, ntiles);
 
-  const float* q = a.q + (size_t)r * a.d + (size_t)h * hd;
-  for (int i = threadIdx.x; i < hd; i += kThreads) qs[i] = (double)q[i];
+  const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * HD;
+  const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);   // [Sp/64][HD/4][64] float4
+  const float* vb = a.vc + head_off;                                      // [Sp][HD]
+  const double sqrt_hd = sqrt((double)HD);
+
+  TileRegs<HD> cur;
+  if (tile0 < tile1) load_tile<HD>(cur, kt, vb, tile0, kvlen, w, lane);   // first tile in flight
+  const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
+  for (int i = threadIdx.x; i < HD / 4; i += kThreads) qs4[i] = q4[i];
   __syncthreads();
-
-  const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * hd;
-  const float* kt = a.kc + head_off;   // tiles [Sp/64][hd][64]
-  const float* vb = a.vc + head_off;   // rows [Sp][hd]
-  const int dq = hd >> 2;
-  const double inv_sqrt_hd_div = sqrt((double)hd);
 
   double m_run = -INFINITY, l_run = 0.0;
   double o[DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.0;
+  for (int k = 0; k < DPL; ++k) o[k] = 0.0;
 
-  for (int j0 = start; j0 < end; j0 += kTile) {
-    const float* tile = kt + (size_t)(j0 >> 6) * hd * kTile;
-    double s = 0.0;
-    for (int i = w * dq; i < (w + 1) * dq; ++i) s = fma(qs[i], (double)tile[i * kTile + lane], s);
-    sp[w][lane] = s;
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int j0 = tile * kTile;
+    // ---- partial scores over this wave's dimensions (4 independent chains)
+    double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+      const float4 qv = qs4[w * KQ + i];
+      s4[0] = fma((double)qv.x, (double)cur.k[i].x, s4[0]);
+      s4[1] = fma((double)qv.y, (double)cur.k[i].y, s4[1]);
+      s4[2] = fma((double)qv.z, (double)cur.k[i].z, s4[2]);
+      s4[3] = fma((double)qv.w, (double)cur.k[i].w, s4[3]);
+    }
+    sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     __syncthreads();
-    const int j = j0 + lane;
-    const bool valid = j < end;
-    double sc = ((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane];
-    sc = sc / inv_sqrt_hd_div;
-    const double mt = wave_max(valid ? sc : -INFINITY);
-    const double m_new = fmax(m_run, mt);
+    // ---- online softmax (every wave derives the same m, l from the same scores)
+    const bool valid = j0 + lane < kvlen;
+    const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
+    const double m_new = fmax(m_run, wave_max(valid ? sc : -INFINITY));
     const double scale = exp(m_run - m_new);   // 0 on the first tile (m_run = -inf)
     const double e = valid ? exp(sc - m_new) : 0.0;
+    if (w == 0) es[lane] = e;
     l_run = l_run * scale + wave_sum(e);
+    __syncthreads();
+    // ---- weighted values of this wave's 16 positions
+    double oo[DPL][2];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] *= scale;
-    const int jend = min(16 * w + 16, end - j0);
-    for (int jj = 16 * w; jj < 16 * w + 16; ++jj) {
-      const double ej = __shfl(e, jj, kWave);
-      if (jj < jend) {
-        const float* vrow = vb + (size_t)(j0 + jj) * hd;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) {
-          const int i = lane * DPL + k;
-          if (i < hd) o[k] = fma(ej, (double)vrow[i], o[k]);
-        }
-      }
+    for (int k = 0; k < DPL; ++k) {
+      oo[k][0] = o[k] * scale;
+      oo[k][1] = 0.0;
     }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const double ej = es[16 * w + jj];   // 0 past the history
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) oo[k][jj & 1] = fma(ej, (double)cur.v[jj][k], oo[k][jj & 1]);
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = oo[k][0] + oo[k][1];
     m_run = m_new;
-    __syncthreads();   // sp is rewritten by the next tile
+    if (tile + 1 < tile1) {
+      load_tile<HD>(cur, kt, vb, tile + 1, kvlen, w, lane);
+      __syncthreads();   // sp / es are rewritten by the next tile
+    }
   }
 
 #pragma unroll
@@ -95,16 +188,21 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int c
     if (i < hd) ow[w][i] = o[k];
   }
   __syncthreads();
-  if (w != 0) return;
+  const size_t unit = (size_t)r * a.H + h;
   if (nchunk == 1) {
-    float* out = a.out + (size_t)r * a.d + (size_t)h * hd;
+    if (w == 0) {
+      float* out = a.out + (size_t)r * a.d + (size_t)h * hd;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      const int i = lane * DPL + k;
-      if (i < hd) out[i] = (float)((((ow[0][i] + ow[1][i]) + ow[2][i]) + ow[3][i]) / l_run);
+      for (int k = 0; k < DPL; ++k) {
+        const int i = lane * DPL + k;
+        if (i < hd) out[i] = (float)((((ow[0][i] + ow[1][i]) + ow[2][i]) + ow[3][i]) / l_run);
+      }
     }
-  } else {
-    double* part = a.part + (((size_t)r * a.H + h) * nchunk + c) * (hd + 2);
+    return;
+  }
+  // ---- split head: publish this chunk's partial
+  double* part = a.part + (unit * nchunk + c) * (hd + 2);
+  if (w == 0) {
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
       const int i = lane * DPL + k;
@@ -114,30 +212,22 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int c
       part[hd] = m_run;
       part[hd + 1] = l_run;
     }
+    if (FUSED) __threadfence();   // release: the partial is visible device-wide before the ticket
   }
+  if (!FUSED) return;             // a separate merge launch follows
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    is_last = atomicAdd(&a.ticket[unit], 1) == nchunk - 1;
+    if (is_last) __threadfence();   // acquire: see every other chunk's partial
+  }
+  __syncthreads();
+  if (!is_last) return;
+  merge_unit(a, r, h, nchunk);
+  if (threadIdx.x == 0) a.ticket[unit] = 0;   // ready for the next launch
 }
 
-// Merge the chunk partials of one (row, head): o = sum_c o_c e^(m_c - m) / sum_c l_c e^(m_c - m).
-__global__ void __launch_bounds__(64) k_attn_merge(AttnArgs a, int nchunk) {
-  const int h = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
-  const int hd = a.hd;
-  const double* part = a.part + ((size_t)r * a.H + h) * nchunk * (hd + 2);
-  double m = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) m = fmax(m, part[(size_t)c * (hd + 2) + hd]);
-  double l = 0.0;
-  for (int c = 0; c < nchunk; ++c) {
-    const double* pc = part + (size_t)c * (hd + 2);
-    if (pc[hd + 1] > 0.0) l += pc[hd + 1] * exp(pc[hd] - m);
-  }
-  float* out = a.out + (size_t)r * a.d + (size_t)h * hd;
-  for (int i = lane; i < hd; i += 64) {
-    double o = 0.0;
-    for (int c = 0; c < nchunk; ++c) {
-      const double* pc = part + (size_t)c * (hd + 2);
-      if (pc[hd + 1] > 0.0) o += pc[i] * exp(pc[hd] - m);
-    }
-    out[i] = (float)(o / l);
-  }
+__global__ void __launch_bounds__(kThreads) k_attn_merge(AttnArgs a, int nchunk) {
+  merge_unit(a, blockIdx.y, blockIdx.x, nchunk);
 }
 
 }  // namespace
@@ -146,24 +236,27 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int maxkv = a.pos + a.n_tok;              // longest history among the rows
   const int tiles = (maxkv + kTile - 1) / kTile;
   const int units = a.rows * a.H;
-  int nchunk = 1;
-  if (units < 512) {
-    nchunk = (512 + units - 1) / units;
-    if (nchunk > tiles) nchunk = tiles;
-    while (nchunk > 1 && (size_t)units * nchunk > (size_t)kMaxAttnParts) --nchunk;
+  int per = tiles;                                // tiles per chunk
+  if (units < kSplitBelow) {
+    // about 256 workgroups: one or two tiles each (measured best at the 7B decode shape)
+    per = (units * tiles) / 256;
+    if (per < 1) per = 1;
+    while ((size_t)units * ((tiles + per - 1) / per) > (size_t)kMaxAttnParts) ++per;
   }
-  const int chunk = ((tiles + nchunk - 1) / nchunk) * kTile;
-  nchunk = (maxkv + chunk - 1) / chunk;
+  const int nchunk = (tiles + per - 1) / per;
   dim3 grid(nchunk, a.H, a.rows);
-  if (a.hd <= 64)
-    hipLaunchKernelGGL((k_attn<1>), grid, dim3(kThreads), 0, s, a, nchunk, chunk);
-  else if (a.hd <= 128)
-    hipLaunchKernelGGL((k_attn<2>), grid, dim3(kThreads), 0, s, a, nchunk, chunk);
-  else
-    hipLaunchKernelGGL((k_attn<4>), grid, dim3(kThreads), 0, s, a, nchunk, chunk);
+  switch (a.hd) {
+#define LD_ATTN_CASE(HD) \
+    case HD: hipLaunchKernelGGL((k_attn<HD, kFusedMerge>), grid, dim3(kThreads), 0, s, a, nchunk, per); break;
+    LD_ATTN_CASE(16) LD_ATTN_CASE(32) LD_ATTN_CASE(48) LD_ATTN_CASE(64) LD_ATTN_CASE(80) LD_ATTN_CASE(96)
+    LD_ATTN_CASE(112) LD_ATTN_CASE(128) LD_ATTN_CASE(144) LD_ATTN_CASE(160) LD_ATTN_CASE(176)
+    LD_ATTN_CASE(192) LD_ATTN_CASE(208) LD_ATTN_CASE(224) LD_ATTN_CASE(240) LD_ATTN_CASE(256)
+#undef LD_ATTN_CASE
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nchunk == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.rows), dim3(64), 0, s, a, nchunk);
+  if (e != hipSuccess || nchunk == 1 || kFusedMerge) return e;
+  hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.rows), dim3(kThreads), 0, s, a, nchunk);
   return hipGetLastError();
 }
 

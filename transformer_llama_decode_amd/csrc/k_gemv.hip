@@ -6,13 +6,20 @@
 //    it: the Q/K/V, W1/W3 and classifier projections) is staged once per
 //    workgroup in LDS as fp32, exactly as the pages' engine stores it;
 //  * each wave owns RW rows at a time; its 64 lanes stride across K with 16-byte
-//    loads, so one wave load instruction covers 1 KiB of a row and up to RW*U
-//    loads are in flight per lane; the grid strides over row groups;
+//    loads, so one wave load instruction covers 1 KiB of a row and RW*U loads
+//    are in flight per lane; the grid strides over row groups;
+//  * when the weights do not fit the 256 MB Infinity Cache the loads are
+//    non-temporal (streamed past the caches): on MI355X this lifts a pure read
+//    stream from ~6.2 to ~7.1 TB/s; small models keep normal loads so their
+//    weights stay cache-resident from one token to the next;
 //  * products of two fp32 values are exact in fp64, so every dot product is
 //    accumulated in fp64 and rounded once to fp32: the stored value is the
 //    correctly rounded dot product, independent of the summation order.  At
-//    ~2 fp64 VALU ops per weight this stays far below the ALU roofline;
-//  * lane partial sums are combined with a fixed-order xor butterfly;
+//    ~2 fp64 VALU ops per weight this uses ~10% of the VALU at full bandwidth;
+//  * lane partial sums are combined with a fixed-order xor butterfly, then lane
+//    i finishes row i of the group: everything an epilogue reads (the residual
+//    row, the rotary cos/sin row) is fetched before the dot product so the
+//    wave never waits on memory between row groups;
 //  * epilogues are fused: rotary embedding + KV-cache write for Q/K/V, residual
 //    add for Wo and W2, the SwiGLU gate for W1/W3, and per-block arg-max
 //    partials for the classifier.
@@ -25,9 +32,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kMaxBlocks = 1024;   // 4 workgroups per CU on 256 CUs; the grid strides beyond
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_CLS = 3 };
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ float4 ld_w(const float4* p) {
+  if (NT) {
+    const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+  }
+  return *p;
+}
 
 // Stage x[0..K) into LDS; with a gain, replace it by RMSNorm(x) * gain rounded to fp32.
 __device__ void stage_input(float* xs, const float* __restrict__ x, const float* __restrict__ gain,
@@ -68,30 +85,42 @@ __device__ void stage_input(float* xs, const float* __restrict__ x, const float*
   __syncthreads();
 }
 
-// acc[r] += sum over this lane's slice of K of W_r . x  for NR row pointers.
+template <int NR, int U, bool NT>
+__device__ __forceinline__ void load_batch(float4 (&w)[U][NR], const float4* (&rows)[NR], int it,
+                                           int lane) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[u][r] = ld_w<NT>(rows[r] + (it + u) * kWave + lane);
+}
+
 template <int NR, int U>
+__device__ __forceinline__ void fma_batch(const float4 (&w)[U][NR], const float4* xs4, int it, int lane,
+                                          double (&acc)[NR]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float4 xv = xs4[(it + u) * kWave + lane];
+    const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = dot4(w[u][r], x0, x1, x2, x3, acc[r]);
+  }
+}
+
+// acc[r] += sum over this lane's slice of K of W_r . x  for NR row pointers,
+// starting at float4 column block `it` (the blocks before it are done already).
+template <int NR, int U, bool NT>
 __device__ __forceinline__ void dot_rows(const float4* (&rows)[NR], const float4* xs4, int K4,
-                                         int lane, double (&acc)[NR]) {
+                                         int lane, double (&acc)[NR], int it) {
   const int nfull = K4 >> 6;
-  int it = 0;
   for (; it + U <= nfull; it += U) {
     float4 w[U][NR];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < NR; ++r) w[u][r] = rows[r][(it + u) * kWave + lane];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float4 xv = xs4[(it + u) * kWave + lane];
-      const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = dot4(w[u][r], x0, x1, x2, x3, acc[r]);
-    }
+    load_batch<NR, U, NT>(w, rows, it, lane);
+    fma_batch<NR, U>(w, xs4, it, lane, acc);
   }
   for (; it < nfull; ++it) {
     float4 w[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) w[r] = rows[r][it * kWave + lane];
+    for (int r = 0; r < NR; ++r) w[r] = ld_w<NT>(rows[r] + it * kWave + lane);
     const float4 xv = xs4[it * kWave + lane];
     const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
 #pragma unroll
@@ -102,21 +131,29 @@ __device__ __forceinline__ void dot_rows(const float4* (&rows)[NR], const float4
     const float4 xv = xs4[j];
     const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = dot4(rows[r][j], x0, x1, x2, x3, acc[r]);
+    for (int r = 0; r < NR; ++r) acc[r] = dot4(ld_w<NT>(rows[r] + j), x0, x1, x2, x3, acc[r]);
   }
 }
 
-template <int EPI, int RW, int U>
+// value of acc[i] where i = this lane's index (compile-time unrolled select)
+template <int N>
+__device__ __forceinline__ double pick(const double (&acc)[N], int i) {
+  double v = 0.0;
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (k == i) v = acc[k];
+  return v;
+}
+
+template <int EPI, int RW, int U, bool NT>
 __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   extern __shared__ float xs[];
   __shared__ double red[kWavesPerBlock];
   __shared__ float best_v[kWavesPerBlock];
   __shared__ int best_i[kWavesPerBlock];
+  __shared__ float rope_cs[2 * 128];          // cos, sin row of this position (hd <= 256)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = a.K, K4 = K >> 2, N = a.N;
-
-  stage_input(xs, a.x, a.gain, K, a.eps, red);
-  const float4* xs4 = reinterpret_cast<const float4*>(xs);
 
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * RW : RW;
   const int ngroups = (N + RW - 1) / RW;
@@ -125,9 +162,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   int bi = 0x7fffffff;
   bool nonfinite = false;
 
-  for (int grp = blockIdx.x * kWavesPerBlock + wave; grp < ngroups; grp += wstride) {
-    const int r0 = grp * RW;
-    const float4* rows[NR];
+  auto set_rows = [&](const float4* (&rows)[NR], int r0) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const int r = min(r0 + i, N - 1);   // rows past N are computed and dropped
@@ -139,15 +174,50 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         rows[i] = reinterpret_cast<const float4*>(a.W + (size_t)r * K);
       }
     }
+  };
+
+  // The weights do not depend on the input vector: issue the first batch of
+  // this wave's loads before staging (and normalising) x, so the prologue
+  // overlaps the first HBM round trip.
+  int grp = blockIdx.x * kWavesPerBlock + wave;
+  const float4* rows[NR];
+  set_rows(rows, grp * RW);
+  float4 wpre[U][NR];
+  const bool pre = grp < ngroups && (K4 >> 6) >= U;
+  if (pre) load_batch<NR, U, NT>(wpre, rows, 0, lane);
+
+  if (EPI == EPI_QKV) {
+    const int half = a.hd >> 1;
+    for (int i = threadIdx.x; i < half; i += kThreads) {
+      rope_cs[i] = a.rcos[(size_t)a.pos * half + i];
+      rope_cs[128 + i] = a.rsin[(size_t)a.pos * half + i];
+    }
+  }
+  stage_input(xs, a.x, a.gain, K, a.eps, red);
+  const float4* xs4 = reinterpret_cast<const float4*>(xs);
+
+  for (bool first = true; grp < ngroups; grp += wstride, first = false) {
+    const int r0 = grp * RW;
+    if (!first) set_rows(rows, r0);
+    // lane i finishes row r0 + i: fetch what its epilogue reads now
+    const int my_r = r0 + lane;
+    const bool mine = lane < RW && my_r < N;
+    float resid_in = 0.f;
+    if (EPI == EPI_RESID && mine) resid_in = a.resid[my_r];
+
     double acc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.0;
-    dot_rows<NR, U>(rows, xs4, K4, lane, acc);
+    int it0 = 0;
+    if (first && pre) {
+      fma_batch<NR, U>(wpre, xs4, 0, lane, acc);
+      it0 = U;
+    }
+    dot_rows<NR, U, NT>(rows, xs4, K4, lane, acc, it0);
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
 
     if (EPI == EPI_CLS) {
-      // every lane holds all RW sums; fold them into the wave's running best
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const int r = r0 + i;
@@ -155,49 +225,42 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
           const float y = (float)acc[i];
           if (!isfinite(y)) nonfinite = true;
           argmax_merge(bv, bi, y, r);
-          if (a.logits != nullptr && lane == i) a.logits[r] = y;
         }
       }
+      if (a.logits != nullptr && mine) a.logits[my_r] = (float)pick(acc, lane);
       continue;
     }
-    if (lane != 0) continue;
+    if (!mine) continue;
     if (EPI == EPI_QKV) {
-      const int d = a.d, hd = a.hd, half = hd >> 1;
-#pragma unroll
-      for (int i = 0; i < RW; i += 2) {
-        const int r = r0 + i;
-        if (r >= N) break;
-        float y0 = (float)acc[i], y1 = (float)acc[i + 1];
-        const int sec = r / d, c = r - sec * d, h = c / hd, ii = c - h * hd;
-        if (sec < 2) {
-          const int t = a.pos * half + (ii >> 1);
-          rope_pair(y0, y1, a.rcos[t], a.rsin[t], y0, y1);
-        }
-        if (sec == 0) {
-          a.q_out[c] = y0;
-          a.q_out[c + 1] = y1;
-        } else if (sec == 1) {
-          float* kh = a.kc + (size_t)h * a.seq_pad * hd;
-          kh[ktile_index(a.pos, ii, hd)] = y0;
-          kh[ktile_index(a.pos, ii + 1, hd)] = y1;
-        } else {
-          float* vrow = a.vc + ((size_t)h * a.seq_pad + a.pos) * hd;
-          vrow[ii] = y0;
-          vrow[ii + 1] = y1;
-        }
+      // lane i (even) rotates the pair (r0+i, r0+i+1); odd lanes hold the partner
+      if (lane & 1) continue;
+      float y0 = (float)pick(acc, lane), y1 = (float)pick(acc, lane + 1);
+      const int d = a.d, hd = a.hd;
+      const int sec = my_r / d, c = my_r - sec * d, h = c / hd, ii = c - h * hd;
+      if (sec < 2) rope_pair(y0, y1, rope_cs[ii >> 1], rope_cs[128 + (ii >> 1)], y0, y1);
+      if (sec == 0) {
+        a.q_out[c] = y0;
+        a.q_out[c + 1] = y1;
+      } else if (sec == 1) {
+        float* kh = a.kc + (size_t)h * a.seq_pad * hd;
+        kh[ktile_index(a.pos, ii, hd)] = y0;
+        kh[ktile_index(a.pos, ii + 1, hd)] = y1;
+      } else {
+        float* vrow = a.vc + ((size_t)h * a.seq_pad + a.pos) * hd;
+        vrow[ii] = y0;
+        vrow[ii + 1] = y1;
       }
     } else if (EPI == EPI_RESID) {
-#pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        const int r = r0 + i;
-        if (r < N) a.resid[r] = a.resid[r] + (float)acc[i];
-      }
+      a.resid[my_r] = resid_in + (float)pick(acc, lane);
     } else if (EPI == EPI_SWIGLU) {
+      double h1 = 0.0, h3 = 0.0;
 #pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        const int r = r0 + i;
-        if (r < N) a.g_out[r] = swiglu((float)acc[i], (float)acc[RW + i]);
-      }
+      for (int k = 0; k < RW; ++k)
+        if (k == lane) {
+          h1 = acc[k];
+          h3 = acc[RW + k];
+        }
+      a.g_out[my_r] = swiglu((float)h1, (float)h3);
     }
   }
 
@@ -218,32 +281,41 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   }
 }
 
-int grid_for(int N, int rw) {
-  const int groups = (N + rw - 1) / rw;
+template <int EPI, int RW, int U, bool NT>
+hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blocks_out) {
+  const int groups = (a.N + RW - 1) / RW;
   int blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  return blocks < kMaxBlocks ? blocks : kMaxBlocks;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks_out) *blocks_out = blocks;
+  const size_t shmem = (size_t)a.K * sizeof(float);
+  hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT>), dim3(blocks), dim3(kThreads), shmem, s, a);
+  return hipGetLastError();
 }
+
+// Streamed (non-temporal) loads once the model's weights are too big to stay
+// in the Infinity Cache from one token to the next.
+bool streamed(const GemvArgs& a) { return a.stream; }
 
 template <int EPI, int RW, int U>
 hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
-  const int blocks = grid_for(a.N, RW);
-  if (blocks_out) *blocks_out = blocks;
-  const size_t shmem = (size_t)a.K * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<EPI, RW, U>), dim3(blocks), dim3(kThreads), shmem, s, a);
-  return hipGetLastError();
+  constexpr int kMaxBlocks = 512;   // 2 resident workgroups per CU on 256 CUs; the grid strides beyond
+  if (streamed(a)) return launch_cfg<EPI, RW, U, true>(a, kMaxBlocks, s, blocks_out);
+  return launch_cfg<EPI, RW, U, false>(a, kMaxBlocks, s, blocks_out);
 }
 
 }  // namespace
 
-hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s) { return launch<EPI_QKV, 4, 4>(a, s); }
+// Shapes measured best on MI355X at the 7B sizes (rows per wave RW, batches
+// of U 16-byte loads per row in flight).
+hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s) { return launch<EPI_QKV, 2, 8>(a, s); }
 hipError_t launch_gemv_resid(const GemvArgs& a, hipStream_t s) {
-  return launch<EPI_RESID, 4, 4>(a, s);
+  return launch<EPI_RESID, 2, 8>(a, s);
 }
 hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s) {
-  return launch<EPI_SWIGLU, 2, 4>(a, s);
+  return launch<EPI_SWIGLU, 1, 8>(a, s);
 }
 hipError_t launch_gemv_cls(const GemvArgs& a, int* nparts, hipStream_t s) {
-  return launch<EPI_CLS, 4, 4>(a, s, nparts);
+  return launch<EPI_CLS, 2, 8>(a, s, nparts);
 }
 
 }  // namespace ld

@@ -13,9 +13,10 @@
 //   Wcls   [V][d]                 only when untied
 //   gain_final [d]
 //   rope_cos, rope_sin [S][hd/2]  fp32, from double on the host
-//   K cache [L][Bmax][H][Sp/64][hd][64]  (Sp = S rounded up to 64): each 64-position
-//                                 tile stored dimension-major, so a wave reading one
-//                                 dimension of 64 consecutive positions is coalesced
+//   K cache [L][Bmax][H][Sp/64][hd/4][64][4]  (Sp = S rounded up to 64): in each
+//                                 64-position tile, a float4 holds 4 dimensions of one
+//                                 position and 64 consecutive positions of the same 4
+//                                 dimensions are contiguous (1 KiB per wave load)
 //   V cache [L][Bmax][H][Sp][hd]  position-major rows
 //   activations for up to R rows: x, xn, q, att [R][d]; g [R][f]
 //   attention partials, arg-max partials, token buffers, error flag
@@ -38,7 +39,7 @@ enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS =
 struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
-  size_t x, xn, q, att, g, attn_part, arg_val, arg_idx, tok, next, err;
+  size_t x, xn, q, att, g, attn_part, attn_ticket, arg_val, arg_idx, tok, next, err;
   size_t total;
   int rows;            // R: activation rows per forward pass
   int seq_pad;         // Sp
@@ -52,6 +53,7 @@ struct GemvArgs {
   double eps;
   const float* W;      // rows of K floats
   int N, K;
+  bool stream;         // non-temporal weight loads (weights larger than the Infinity Cache)
   // QKV epilogue
   float* q_out;
   float* kc;           // K cache of (layer, sequence 0)
@@ -82,6 +84,7 @@ struct AttnArgs {
   const float* vc;     // V cache of this layer, sequence 0
   float* out;          // [rows][d]
   double* part;        // partial (o[hd], m, l) per (row, head, chunk)
+  int* ticket;         // per (row, head) arrival counters, zero between launches
   int rows, n_tok, pos, d, H, hd, seq_pad, bmax;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

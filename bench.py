@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/sec at batch 1 (15M/44M/7B-shape fp32) + achieved HBM GB/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 W13_SOURCES = ["transformer_llama_decode_amd/csrc/k_gemv.hip", "transformer_llama_decode_amd/csrc/dev_common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w13_gemv_7b.json")
 
@@ -95,12 +96,19 @@ def cpu_baseline(w, n_steps):
     }
 
 
+def gemm_flops_per_step(cfg, batch):
+    """Algorithmic flops of every projection of one decode step for `batch` rows."""
+    d, f, V, L = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers
+    return 2 * batch * (L * (4 * d * d + 3 * d * f) + V * d)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="C5")
+    ap.add_argument("--workload", default="C5",
+                    help="C5 (default: 7B shape, batch 1); also C1, C2, C3 (batch 256), C4, C4b32")
     ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -134,13 +142,14 @@ def main():
 
     from transformer_llama_decode_amd.configs import WORKLOADS
     from transformer_llama_decode_amd.model import LlamaDecoder, synth_prompt
-    from transformer_llama_decode_amd._lib import LD_K_W13
+    from transformer_llama_decode_amd import _lib
 
     w = WORKLOADS[args.workload]
     cfg = w.model
-    B = 1
+    B = w.batch
     P = max(w.prompt_len, 1)
-    if P + max(args.steps, args.warmup) > cfg.max_seq:
+    steps = min(args.steps, w.end_pos - P)
+    if P + max(steps, args.warmup) > cfg.max_seq:
         sys.exit("steps + prompt exceed max_seq %d" % cfg.max_seq)
     dev = torch.device("cuda", 0)
     t0 = time.time()
@@ -148,18 +157,21 @@ def main():
     torch.cuda.synchronize()
     log("init %.1fs (%s, arena %.2f GB)" % (time.time() - t0, w.name, gm.arena.numel() / 1e9))
 
-    prompt = synth_prompt(w.prompt_seed, 0, w.prompt_len) if w.prompt_len else np.array([w.start_token], np.int32)
+    if w.prompt_len:
+        prompt = np.stack([synth_prompt(w.prompt_seed, b, w.prompt_len) for b in range(B)])
+    else:
+        prompt = np.full((B, 1), w.start_token, np.int32)
     bufs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
     # prefill (timed on its own)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if w.prompt_len:
-        gm.prefill(prompt[None, :], next_out=bufs[0])
+        gm.prefill(prompt, next_out=bufs[0])
     else:
-        gm.decode_step(prompt, next_out=bufs[0])
+        gm.decode_step(prompt[:, 0], next_out=bufs[0])
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t0
-    log("prefill %d tokens: %.1f ms" % (len(prompt), prefill_s * 1e3))
+    log("prefill %d x %d tokens: %.1f ms" % (B, prompt.shape[1], prefill_s * 1e3))
 
     def run(k, tok):
         for i in range(k):
@@ -176,41 +188,80 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    run(args.steps, start_tok)
+    run(steps, start_tok)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_s = ev0.elapsed_time(ev1) / 1e3
-    # The dominant kernel, timed with HIP events recorded around each of its
-    # launches on the library's stream, over the same positions again (event
-    # records stall the stream for a few microseconds, so they stay out of the
-    # pass that gives the throughput).
+    # Kernels timed with HIP events recorded around each of their launches on
+    # the library's stream, over the same positions again (event records stall
+    # the stream for a few microseconds, so they stay out of the throughput pass).
+    classes = [_lib.LD_K_W13] if B == 1 else [_lib.LD_K_QKV, _lib.LD_K_WO, _lib.LD_K_W13,
+                                              _lib.LD_K_W2, _lib.LD_K_CLS]
     gm.set_pos(P)
-    gm.profile(LD_K_W13, True)
-    run(args.steps, start_tok)
-    w13_ms, w13_n = gm.profile_read(LD_K_W13)
-    gm.profile(LD_K_W13, False)
+    for k in classes:
+        gm.profile(k, True)
+    run(steps, start_tok)
+    kt = {k: gm.profile_read(k) for k in classes}
+    for k in classes:
+        gm.profile(k, False)
     status = gm.status()
     if status != 0:
         sys.exit("device reported error %d during the run" % status)
 
     elapsed = wall
-    tok_s = B * args.steps / elapsed
-    avg_bytes = sum(step_bytes(cfg, p, B) for p in range(P, P + args.steps)) / args.steps
-    w13_bytes = w13_launch_bytes(cfg)
-    achieved = w13_bytes / (w13_ms * 1e-3) / 1e9 if w13_ms > 0 else None
-    traffic = measured_traffic()
-    log("decode: %.2f ms/step, %.1f tok/s, %.0f GB/s over the step; W13 %.3f ms x %d -> %.0f GB/s"
-        % (elapsed / args.steps * 1e3, tok_s, avg_bytes * tok_s / 1e9, w13_ms, w13_n, achieved or 0))
+    tok_s = B * steps / elapsed
+    avg_bytes = sum(step_bytes(cfg, p, B) for p in range(P, P + steps)) / steps
+    if B == 1:
+        w13_ms, w13_n = kt[_lib.LD_K_W13]
+        w13_bytes = w13_launch_bytes(cfg)
+        achieved = w13_bytes / (w13_ms * 1e-3) / 1e9 if w13_ms > 0 else None
+        roof = {
+            "bound": "hbm",
+            "kernel": "W1/W3 + SwiGLU GEMV (k_gemv<EPI_SWIGLU>), batch 1",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+            "traffic": measured_traffic() if w.name == "C5" else None,
+            "bytes_per_launch": w13_bytes,
+            "avg_launch_ms": round(w13_ms, 5),
+            "launches": w13_n,
+        }
+        log("decode: %.3f ms/step, %.1f tok/s, %.0f GB/s over the step; W13 %.4f ms x %d -> %.0f GB/s"
+            % (elapsed / steps * 1e3, tok_s, avg_bytes * tok_s / 1e9, w13_ms, w13_n, achieved or 0))
+    else:
+        gemm_s = sum(ms * n for ms, n in kt.values()) / 1e3 / steps   # GEMM seconds per step
+        flops = gemm_flops_per_step(cfg, B)
+        achieved = flops / gemm_s / 1e12
+        roof = {
+            "bound": "mfma",
+            "kernel": "fp32 MFMA projections (k_gemm, v_mfma_f32_32x32x2_f32), batch %d" % B,
+            "achieved": round(achieved, 2),
+            "peak": MFMA_F32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_step": flops,
+            "gemm_ms_per_step": round(gemm_s * 1e3, 4),
+            "per_class_ms": {name: round(kt[k][0], 5) for name, k in
+                             [("qkv", _lib.LD_K_QKV), ("wo", _lib.LD_K_WO), ("w13", _lib.LD_K_W13),
+                              ("w2", _lib.LD_K_W2), ("cls", _lib.LD_K_CLS)]},
+            "whole_step_frac": round(flops * tok_s / B / 1e12 / MFMA_F32_PEAK_TFLOPS, 4),
+        }
+        log("decode: %.3f ms/step, %.0f tok/s; GEMMs %.3f ms/step -> %.1f TFLOP/s (%.1f%% of fp32 MFMA peak)"
+            % (elapsed / steps * 1e3, tok_s, gemm_s * 1e3, achieved, 100 * achieved / MFMA_F32_PEAK_TFLOPS))
+    roof["timing"] = ("HIP event pairs on the library's stream around every launch, in a second "
+                      "pass over the timed positions")
 
     rec = {
         "metric": METRIC,
         "value": round(tok_s, 3),
         "unit": "tok/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -219,30 +270,17 @@ def main():
         "config": {
             "workload": "%s: %s" % (w.name, w.description),
             "batch": B,
-            "positions": "%d..%d" % (P, P + args.steps - 1),
-            "prompt_tokens": int(len(prompt)),
+            "positions": "%d..%d" % (P, P + steps - 1),
+            "prompt_tokens": int(prompt.shape[1]) if w.prompt_len else 0,
             "seed": w.model_seed,
         },
-        "hbm_gbps_step": round(avg_bytes * tok_s / 1e9, 1),
-        "hbm_frac_step": round(avg_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_gbps_step": round(avg_bytes * tok_s / B / 1e9, 1),
+        "hbm_frac_step": round(avg_bytes * tok_s / B / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(avg_bytes),
-        "gpu_event_ms_per_step": round(gpu_s / args.steps * 1e3, 4),
+        "gpu_event_ms_per_step": round(gpu_s / steps * 1e3, 4),
         "prefill_ms": round(prefill_s * 1e3, 2),
-        "prefill_tok_s": round(len(prompt) / prefill_s, 1),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "W1/W3 + SwiGLU GEMV (k_gemv<EPI_SWIGLU>), batch 1",
-            "achieved": round(achieved, 1) if achieved else None,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-            "traffic": traffic,
-            "bytes_per_launch": w13_bytes,
-            "avg_launch_ms": round(w13_ms, 5),
-            "launches": w13_n,
-            "timing": "HIP event pairs on the library's stream around every launch, in a "
-                      "second pass over the timed positions",
-        },
+        "prefill_tok_s": round(B * prompt.shape[1] / prefill_s, 1),
+        "roofline": roof,
     }
     gm.close()
     del gm

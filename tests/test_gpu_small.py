@@ -158,6 +158,28 @@ def test_batched_lockstep_matches_each_sequence_alone(dev, cfg, seed):
     gm.close()
 
 
+@pytest.mark.parametrize("cfg,seed", [(TINY, 11), (SMALL, 12)])
+def test_many_row_prefill_every_logit(dev, cfg, seed):
+    # more than 256 rows per forward pass: the LDS-tiled MFMA GEMM path
+    # (smaller row counts take the split-K path exercised above)
+    _say("many-row prefill", cfg)
+    B = cfg.max_batch
+    P = min(cfg.max_seq, 300 // B + 1)
+    assert B * P > 256
+    gm, om = _models(cfg, seed)
+    prompts = np.stack([O.synth_prompt(seed, 10 + b, P, 0, cfg.vocab_size) for b in range(B)])
+    allp = torch.empty((B, P, cfg.vocab_size), dtype=torch.float32, device=dev)
+    nxt = gm.prefill(prompts, logits=allp, all_pos=True)
+    allp = allp.cpu().numpy()
+    nn = nxt.cpu().numpy()
+    for b in range(B):
+        _, ref = _oracle_stream(om, prompts[b], P)
+        for p in range(P):
+            assert_logits(allp[b, p], ref[p], "seq %d pos %d" % (b, p))
+        assert_token(nn[b], ref[P - 1], "seq %d next" % b)
+    gm.close()
+
+
 def test_device_token_feedback_equals_host_tokens(dev):
     cfg, seed = TINY, 3
     gm, _ = _models(cfg, seed)

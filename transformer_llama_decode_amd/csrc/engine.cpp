@@ -411,8 +411,8 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
   int nparts = 0;
   // capacity of the partial arrays (R rows x the GEMM's 2 partials per 128 columns)
   if (cls_rows > m->lay.rows) return LD_E_ARENA;
-  ProfScope ps(m, K_CLS);
   if (cls_rows == 1) {
+    ProfScope ps(m, K_CLS);
     GemvArgs a{};
     a.x = x + (size_t)(n_tok - 1) * d; a.gain = m->at<float>(m->lay.gain_final); a.eps = c.norm_eps;
     a.W = m->at<float>(m->lay.Wcls); a.N = V; a.K = d; a.stream = m->stream_weights;
@@ -433,6 +433,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
     a.logit_rows_per_seq = all_pos ? out_rows_per_seq : 1;
     a.logit_row0 = all_pos ? out_row0 : 0;
     a.part_val = pv; a.part_idx = pi; a.err = err;
+    ProfScope ps(m, K_CLS);
     LD_TRY_HIP(launch_gemm_cls(a, &nparts, m->stream));
   }
   // arg-max of each sequence's last row (every row is a last row unless all_pos)

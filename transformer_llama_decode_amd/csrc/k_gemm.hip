@@ -230,10 +230,190 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 #undef val
 }
 
+// ---------------------------------------------------------------------------
+// Split-K variant for small problems (the layer GEMMs of batched decode): a
+// workgroup owns a 32 x 64 output tile and KW waves split K between them.  Each
+// lane's global float4 loads are already the MFMA operand layout (row lane%32,
+// k offset 4*(lane/32)), so operands go straight from memory to the matrix
+// cores with no LDS staging and no barrier in the K loop; batches of SK_STEPS
+// 8-k groups are issued at once.  The KW partial tiles are summed in LDS in a
+// fixed order (in double), then a shared epilogue reads the finished tile.
+constexpr int SK_STEPS = 8;
+
+template <bool CARRY>
+struct SkAcc {
+  typedef double T;
+};
+template <>
+struct SkAcc<false> {
+  typedef float T;
+};
+
+template <int EPI, bool CARRY>
+__global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
+  typedef typename SkAcc<CARRY>::T PT;
+  extern __shared__ char sk_smem[];
+  PT* red = reinterpret_cast<PT*>(sk_smem);   // [KW][2 tiles][16 regs][64 lanes]
+  const int KW = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int M = a.M, N = a.N, K = a.K;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 64;
+  const int row = lane & 31, kofs = 4 * (lane >> 5);
+  const bool arow_ok = m0 + row < M;
+  const float* Ap = a.A + (size_t)min(m0 + row, M - 1) * K + kofs;
+  const float* W0 = a.W + (size_t)min(n0 + row, N - 1) * K + kofs;
+  const float* W1 = a.W + (size_t)min(n0 + 32 + row, N - 1) * K + kofs;
+  const int k_begin = w * kchunk, k_end = min(K, k_begin + kchunk);
+
+  floatx16 acc0, acc1;
+  double dacc[2][CARRY ? 16 : 1];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    acc0[j] = 0.f;
+    acc1[j] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[0][j] = dacc[1][j] = 0.0;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = k_begin; k0 < k_end; k0 += 8 * SK_STEPS) {
+    float4 av[SK_STEPS], b0[SK_STEPS], b1[SK_STEPS];
+#pragma unroll
+    for (int s = 0; s < SK_STEPS; ++s) {
+      const int kk = k0 + 8 * s;
+      if (kk < k_end) {
+        av[s] = arow_ok ? *reinterpret_cast<const float4*>(Ap + kk) : z4;
+        b0[s] = *reinterpret_cast<const float4*>(W0 + kk);
+        b1[s] = *reinterpret_cast<const float4*>(W1 + kk);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SK_STEPS; ++s) {
+      if (k0 + 8 * s < k_end) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].x, b0[s].x, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].y, b0[s].y, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].z, b0[s].z, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].w, b0[s].w, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].x, b1[s].x, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].y, b1[s].y, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].z, b1[s].z, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].w, b1[s].w, acc1, 0, 0, 0);
+      }
+    }
+    if (CARRY) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        dacc[0][j & (CARRY ? 15 : 0)] += (double)acc0[j];
+        dacc[1][j & (CARRY ? 15 : 0)] += (double)acc1[j];
+        acc0[j] = 0.f;
+        acc1[j] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    red[((w * 2 + 0) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[0][j & (CARRY ? 15 : 0)] : (PT)acc0[j];
+    red[((w * 2 + 1) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[1][j & (CARRY ? 15 : 0)] : (PT)acc1[j];
+  }
+  __syncthreads();
+  // fixed-order sum of the KW partials, rounded once; result kept in slot w = 0
+  for (int e = tid; e < 2 * 16 * 64; e += blockDim.x) {
+    double s = 0.0;
+    for (int ww = 0; ww < KW; ++ww) s += (double)red[ww * 2 * 16 * 64 + e];
+    red[e] = (PT)(float)s;
+  }
+  __syncthreads();
+  // finished value of local output (rl in 0..31, cl in 0..63)
+  auto tile = [&](int rl, int cl) -> float {
+    const int t = cl >> 5, ln = (cl & 31) + 32 * ((rl & 7) >> 2), j = 4 * (rl >> 3) + (rl & 3);
+    return (float)red[(t * 16 + j) * 64 + ln];
+  };
+
+  if (EPI == EPI_RESID) {
+    for (int e = tid; e < 32 * 64; e += blockDim.x) {
+      const int rl = e >> 6, cl = e & 63, r = m0 + rl, c = n0 + cl;
+      if (r < M && c < N) {
+        float* p = a.resid + (size_t)r * N + c;
+        *p = *p + tile(rl, cl);
+      }
+    }
+  } else if (EPI == EPI_QKV) {
+    const int d = a.d, hd = a.hd, half = hd >> 1;
+    for (int e = tid; e < 32 * 32; e += blockDim.x) {
+      const int rl = e >> 5, cl = 2 * (e & 31), r = m0 + rl, col = n0 + cl;
+      if (r >= M || col >= N) continue;
+      float y0 = tile(rl, cl), y1 = tile(rl, cl + 1);
+      const int sec = col / d, c = col - sec * d, h = c / hd, ii = c - h * hd;
+      const int b = r / a.n_tok, p = a.pos + (r - b * a.n_tok);
+      if (sec < 2) {
+        const int t = p * half + (ii >> 1);
+        rope_pair(y0, y1, a.rcos[t], a.rsin[t], y0, y1);
+      }
+      const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * hd;
+      if (sec == 0) {
+        a.q_out[(size_t)r * d + c] = y0;
+        a.q_out[(size_t)r * d + c + 1] = y1;
+      } else if (sec == 1) {
+        a.kc[head_off + ktile_index(p, ii, hd)] = y0;
+        a.kc[head_off + ktile_index(p, ii + 1, hd)] = y1;
+      } else {
+        a.vc[head_off + (size_t)p * hd + ii] = y0;
+        a.vc[head_off + (size_t)p * hd + ii + 1] = y1;
+      }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    for (int e = tid; e < 32 * 32; e += blockDim.x) {
+      const int rl = e >> 5, j = e & 31, r = m0 + rl, fcol = (n0 >> 1) + j;
+      if (r < M && fcol < a.f) a.g_out[(size_t)r * a.f + fcol] = swiglu(tile(rl, j), tile(rl, 32 + j));
+    }
+  } else {   // EPI_CLS: one wave per row, one lane per column
+    const int nparts = gridDim.x;
+    bool bad = false;
+    for (int rl = w; rl < 32; rl += KW) {
+      const int r = m0 + rl, c = n0 + lane;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      if (r < M && c < N) {
+        const float v = tile(rl, lane);
+        if (!isfinite(v)) bad = true;
+        bv = v;
+        bi = c;
+        if (a.logits != nullptr) {
+          const int orow = (r / a.n_tok) * a.logit_rows_per_seq + a.logit_row0 + r % a.n_tok;
+          a.logits[(size_t)orow * N + c] = v;
+        }
+      }
+      wave_argmax(bv, bi, 64);
+      if (lane == 0 && r < M) {
+        a.part_val[(size_t)r * nparts + blockIdx.x] = bv;
+        a.part_idx[(size_t)r * nparts + blockIdx.x] = bi;
+      }
+    }
+    if (bad) atomicOr(a.err, 1);
+  }
+}
+
 template <int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   const int nb = (a.N + 127) / 128;
   auto blocks = [&](int bm) { return ((a.M + bm - 1) / bm) * nb; };
+  if (a.M <= 256 && blocks(a.M > 32 ? 64 : 32) < 256) {
+    // small problem: split K across the waves of a workgroup
+    const int tiles = ((a.N + 63) / 64) * ((a.M + 31) / 32);
+    const int kw_max = a.carry ? 4 : 8;
+    int kw = (1024 + tiles - 1) / tiles;
+    kw = kw < 1 ? 1 : (kw > kw_max ? kw_max : kw);
+    int kchunk = (a.K + kw - 1) / kw;
+    kchunk = (kchunk + 7) / 8 * 8;
+    kw = (a.K + kchunk - 1) / kchunk;
+    dim3 grid((a.N + 63) / 64, (a.M + 31) / 32);
+    const size_t shmem = (size_t)kw * 2 * 16 * 64 * (a.carry ? 8 : 4);
+    if (nparts) *nparts = grid.x;
+    if (a.carry)
+      hipLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(64 * kw), shmem, s, a, kchunk);
+    else
+      hipLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(64 * kw), shmem, s, a, kchunk);
+    return hipGetLastError();
+  }
   int bm;
   if (a.M >= 256 && blocks(128) >= 240)
     bm = 128;

@@ -96,6 +96,56 @@ def cpu_baseline(w, n_steps):
     }
 
 
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_json, out_txt):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the 7B decode
+    bench, and of the plain 2 GiB copy of --copy-calibration) into HBM bytes per
+    W1/W3 GEMV launch, each counter scaled by what it reads for the copy."""
+    import csv
+    import glob
+    import re
+    import statistics
+
+    def per_kernel(d):
+        path = glob.glob(os.path.join(d, "*_counter_collection.csv"))[0]
+        out = {}
+        for r in csv.DictReader(open(path)):
+            name = re.sub(r"\(.*", "", r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                          .replace("void ", "").replace("ld::", ""))
+            out.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)   # KiB -> bytes
+        return {k: statistics.median(v) for k, v in out.items()}
+
+    copy_bytes = 4 << 29
+    f_copy = max(per_kernel(copy_fetch_dir).values())
+    w_copy = max(per_kernel(copy_write_dir).values())
+    k_fetch = copy_bytes / f_copy
+    k_write = copy_bytes / w_copy
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    from transformer_llama_decode_amd.configs import WORKLOADS
+    cfg = WORKLOADS["C5"].model
+    lines = ["kernel  fetch_KiB_raw  write_KiB_raw  traffic_bytes(scaled)  algorithmic_bytes"]
+    w13 = None
+    for name in sorted(fetch, key=lambda n: -fetch[n]):
+        if name not in write:
+            continue
+        t = fetch[name] * k_fetch + write[name] * k_write
+        alg = w13_launch_bytes(cfg) if name.startswith("k_gemv<2,") else None
+        if name.startswith("k_gemv<2,"):
+            w13 = t
+        lines.append("%-28s %14.1f %14.1f %22.0f %18s" % (name, fetch[name] / 1024, write[name] / 1024, t,
+                                                           alg if alg else "-"))
+    rec = {"kernel": "k_gemv<EPI_SWIGLU> (W1/W3 + SwiGLU GEMV), 7B shape, batch 1",
+           "bytes_per_launch": round(w13), "algorithmic_bytes_per_launch": w13_launch_bytes(cfg),
+           "fetch_scale": round(k_fetch, 4), "write_scale": round(k_write, 4),
+           "kernel_source_hash": sources_hash(W13_SOURCES)}
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(out_txt, "w") as fh:
+        fh.write("copy calibration: a 2 GiB device copy reads FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB "
+                 "-> scale fetch x%.4f, write x%.4f\n" % (f_copy / 1024, w_copy / 1024, k_fetch, k_write))
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps(rec))
+
+
 def gemm_flops_per_step(cfg, batch):
     """Algorithmic flops of every projection of one decode step for `batch` rows."""
     d, f, V, L = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers
@@ -113,7 +163,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
+                    help="rocprofv3 --pmc output dirs: FETCH_SIZE and WRITE_SIZE of this bench, "
+                         "then of --copy-calibration; writes the traffic summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, TRAFFIC_FILE,
+                           os.path.join(ROOT, "profiles", "counters_w13_gemv_7b.txt"))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

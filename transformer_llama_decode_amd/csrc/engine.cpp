@@ -125,19 +125,27 @@ struct ld_model {
 
 namespace {
 
-// Records HIP events around one launch of a profiled kernel class.
+// Times one launch of a profiled kernel class with a HIP event pair on the
+// model's stream.  With `in_dispatch` the pair is handed to the launch
+// (hipExtLaunchKernelGGL records it with the kernel's own dispatch, so the
+// interval is the kernel); otherwise the events are recorded around the
+// launches made in this scope.
 struct ProfScope {
   Prof* p;
   hipStream_t s;
   int idx;
-  ProfScope(ld_model* m, int k) : p(&m->prof[k]), s(m->stream), idx(-1) {
+  bool in_dispatch;
+  ProfScope(ld_model* m, int k, bool in_dispatch_ = false)
+      : p(&m->prof[k]), s(m->stream), idx(-1), in_dispatch(in_dispatch_) {
     if (p->on && p->used < kProfPairs) {
       idx = p->used++;
-      hipEventRecord(p->ev[2 * idx], s);
+      if (!in_dispatch) (void)hipEventRecord(p->ev[2 * idx], s);
     }
   }
+  hipEvent_t start() const { return idx >= 0 ? p->ev[2 * idx] : nullptr; }
+  hipEvent_t stop() const { return idx >= 0 ? p->ev[2 * idx + 1] : nullptr; }
   ~ProfScope() {
-    if (idx >= 0) hipEventRecord(p->ev[2 * idx + 1], s);
+    if (idx >= 0 && !in_dispatch) (void)hipEventRecord(p->ev[2 * idx + 1], s);
   }
 };
 
@@ -292,8 +300,9 @@ int layers_gemv(ld_model* m, int pos) {
   float* g = m->at<float>(m->lay.g);
   for (int l = 0; l < c.n_layers; ++l) {
     {
-      ProfScope ps(m, K_QKV);
+      ProfScope ps(m, K_QKV, true);
       GemvArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = x; a.gain = m->layer(l, m->lay.o_gatt); a.eps = c.norm_eps;
       a.W = m->layer(l, m->lay.o_wqkv); a.N = 3 * d; a.K = d; a.stream = m->stream_weights;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
@@ -311,23 +320,26 @@ int layers_gemv(ld_model* m, int pos) {
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
-      ProfScope ps(m, K_WO);
+      ProfScope ps(m, K_WO, true);
       GemvArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = att; a.W = m->layer(l, m->lay.o_wo); a.N = d; a.K = d; a.resid = x;
       a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_resid(a, m->stream));
     }
     {
-      ProfScope ps(m, K_W13);
+      ProfScope ps(m, K_W13, true);
       GemvArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = x; a.gain = m->layer(l, m->lay.o_gffn); a.eps = c.norm_eps;
       a.W = m->layer(l, m->lay.o_w13); a.N = f; a.K = d; a.g_out = g;
       a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_swiglu(a, m->stream));
     }
     {
-      ProfScope ps(m, K_W2);
+      ProfScope ps(m, K_W2, true);
       GemvArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = g; a.W = m->layer(l, m->lay.o_w2); a.N = d; a.K = f; a.resid = x;
       a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_resid(a, m->stream));
@@ -349,8 +361,9 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gatt), rows, d, 1, 0, c.norm_eps,
                                    m->stream));
     {
-      ProfScope ps(m, K_QKV);
+      ProfScope ps(m, K_QKV, true);
       GemmArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = xn; a.W = m->layer(l, m->lay.o_wqkv); a.M = rows; a.N = 3 * d; a.K = d; a.carry = m->carry;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
@@ -368,8 +381,9 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
-      ProfScope ps(m, K_WO);
+      ProfScope ps(m, K_WO, true);
       GemmArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = att; a.W = m->layer(l, m->lay.o_wo); a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
       a.resid = x;
       LD_TRY_HIP(launch_gemm_resid(a, m->stream));
@@ -377,15 +391,17 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gffn), rows, d, 1, 0, c.norm_eps,
                                    m->stream));
     {
-      ProfScope ps(m, K_W13);
+      ProfScope ps(m, K_W13, true);
       GemmArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = xn; a.W = m->layer(l, m->lay.o_w13); a.M = rows; a.N = 2 * f; a.K = d; a.carry = m->carry;
       a.g_out = g; a.f = f;
       LD_TRY_HIP(launch_gemm_swiglu(a, m->stream));
     }
     {
-      ProfScope ps(m, K_W2);
+      ProfScope ps(m, K_W2, true);
       GemmArgs a{};
+      a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = g; a.W = m->layer(l, m->lay.o_w2); a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
       a.resid = x;
       LD_TRY_HIP(launch_gemm_resid(a, m->stream));
@@ -412,8 +428,9 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
   // capacity of the partial arrays (R rows x the GEMM's 2 partials per 128 columns)
   if (cls_rows > m->lay.rows) return LD_E_ARENA;
   if (cls_rows == 1) {
-    ProfScope ps(m, K_CLS);
+    ProfScope ps(m, K_CLS, true);
     GemvArgs a{};
+    a.ev_start = ps.start(); a.ev_stop = ps.stop();
     a.x = x + (size_t)(n_tok - 1) * d; a.gain = m->at<float>(m->lay.gain_final); a.eps = c.norm_eps;
     a.W = m->at<float>(m->lay.Wcls); a.N = V; a.K = d; a.stream = m->stream_weights;
     a.logits = logits ? logits + (size_t)out_row0 * V : nullptr;
@@ -433,7 +450,8 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
     a.logit_rows_per_seq = all_pos ? out_rows_per_seq : 1;
     a.logit_row0 = all_pos ? out_row0 : 0;
     a.part_val = pv; a.part_idx = pi; a.err = err;
-    ProfScope ps(m, K_CLS);
+    ProfScope ps(m, K_CLS, true);
+    a.ev_start = ps.start(); a.ev_stop = ps.stop();
     LD_TRY_HIP(launch_gemm_cls(a, &nparts, m->stream));
   }
   // arg-max of each sequence's last row (every row is a last row unless all_pos)

@@ -409,9 +409,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     const size_t shmem = (size_t)kw * 2 * 16 * 64 * (a.carry ? 8 : 4);
     if (nparts) *nparts = grid.x;
     if (a.carry)
-      hipLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(64 * kw), shmem, s, a, kchunk);
+      hipExtLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(64 * kw), shmem, s, a.ev_start, a.ev_stop,
+                            0, a, kchunk);
     else
-      hipLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(64 * kw), shmem, s, a, kchunk);
+      hipExtLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(64 * kw), shmem, s, a.ev_start,
+                            a.ev_stop, 0, a, kchunk);
     return hipGetLastError();
   }
   int bm;
@@ -425,9 +427,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   if (nparts) *nparts = nb * 2;
 #define LD_GEMM_LAUNCH(WM, MT, THR)                                                             \
   if (a.carry)                                                                                  \
-    hipLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, true>), grid, dim3(THR), 0, s, a);            \
+    hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, true>), grid, dim3(THR), 0, s, a.ev_start, \
+                          a.ev_stop, 0, a);                                                     \
   else                                                                                          \
-    hipLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, false>), grid, dim3(THR), 0, s, a);
+    hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, false>), grid, dim3(THR), 0, s, a.ev_start, \
+                          a.ev_stop, 0, a);
   if (bm == 128) {
     LD_GEMM_LAUNCH(2, 2, 256)
   } else if (bm == 64) {

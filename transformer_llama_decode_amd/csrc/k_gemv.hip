@@ -288,7 +288,11 @@ hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blo
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks_out) *blocks_out = blocks;
   const size_t shmem = (size_t)a.K * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT>), dim3(blocks), dim3(kThreads), shmem, s, a);
+  if (a.ev_start != nullptr)
+    hipExtLaunchKernelGGL((k_gemv<EPI, RW, U, NT>), dim3(blocks), dim3(kThreads), shmem, s, a.ev_start,
+                          a.ev_stop, 0, a);
+  else
+    hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT>), dim3(blocks), dim3(kThreads), shmem, s, a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@
 //   attention partials, arg-max partials, token buffers, error flag
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -54,6 +55,7 @@ struct GemvArgs {
   const float* W;      // rows of K floats
   int N, K;
   bool stream;         // non-temporal weight loads (weights larger than the Infinity Cache)
+  hipEvent_t ev_start, ev_stop;   // when set, recorded by the dispatch itself (timing)
   // QKV epilogue
   float* q_out;
   float* kc;           // K cache of (layer, sequence 0)
@@ -94,6 +96,7 @@ struct GemmArgs {
   const float* W;      // [N][K]
   int M, N, K;
   bool carry;          // fp32 MFMA partial sums carried into fp64 every 32 k
+  hipEvent_t ev_start, ev_stop;   // when set, recorded by the dispatch itself (timing)
   // QKV epilogue
   float* q_out;
   float* kc;

@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--workload", default="C5",
                     help="C5 (default: 7B shape, batch 1); also C1, C2, C3 (batch 256), C4, C4b32")
     ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--eager", action="store_true",
+                    help="time one ld_decode_step call per position instead of the on-device "
+                         "generation loop (ld_generate: the step replayed as a HIP graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
@@ -237,15 +240,23 @@ def main():
             tok = out
         return tok
 
-    tok = run(args.warmup, bufs[0])
+    gen_out = torch.empty((max(steps, args.warmup), B), dtype=torch.int32, device=dev)
+
+    def run_timed(k, tok):
+        if args.eager:
+            return run(k, tok)
+        gm.generate(tok, k, out=gen_out)
+        return gen_out[k - 1]
+
+    tok = run_timed(args.warmup, bufs[0]) if args.warmup > 0 else bufs[0]
     torch.cuda.synchronize()
     gm.set_pos(P)                      # time exactly the workload's positions P .. P+steps-1
-    start_tok = tok
+    start_tok = tok.clone()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    run(steps, start_tok)
+    run_timed(steps, start_tok)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -330,6 +341,8 @@ def main():
             "positions": "%d..%d" % (P, P + steps - 1),
             "prompt_tokens": int(prompt.shape[1]) if w.prompt_len else 0,
             "seed": w.model_seed,
+            "loop": ("host loop of ld_decode_step" if args.eager else
+                     "ld_generate: greedy tokens fed back on the device, one HIP graph replay per position"),
         },
         "hbm_gbps_step": round(avg_bytes * tok_s / B / 1e9, 1),
         "hbm_frac_step": round(avg_bytes * tok_s / B / 1e9 / HBM_PEAK_GBS, 4),

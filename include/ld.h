@@ -93,6 +93,24 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
 int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
                    float* dev_logits, int32_t* dev_next);
 
+/* Greedy generation on the device: n_steps decode positions for `batch`
+ * sequences, each step's arg-max token fed back as the next step's input with
+ * no host round trip -- the pages' generation loop (forward pass, take the most
+ * likely token, feed it back; openai.wiki "llama2.c | Baby LLaMA", section
+ * "Model inference").  tokens[batch] are the first step's input ids, host
+ * (validated) or device memory (tokens_on_device != 0; out-of-range ids as in
+ * ld_decode_step).  Step i's tokens go to dev_out[i * batch + b] (device
+ * memory, n_steps * batch ints, NULL = not written); dev_logits[batch][V]
+ * receives the logits of every step in turn, so it ends with the last step's
+ * (NULL = not written).  The step is captured once as a HIP graph per (batch,
+ * dev_logits) and replayed; a different pair recaptures it.  Same results as
+ * n calls of ld_decode_step fed with their own dev_next, up to the rounding
+ * of the attention split (fixed here by max_seq rather than the position).
+ * Then pos += n_steps.  LD_E_RANGE if pos + n_steps > max_seq; n_steps == 0
+ * does nothing. */
+int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* tokens,
+                int32_t tokens_on_device, float* dev_logits, int32_t* dev_out);
+
 /* Forget the cached sequence: pos := 0. */
 int ld_kv_reset(ld_model* m);
 

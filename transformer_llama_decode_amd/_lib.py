@@ -21,7 +21,7 @@ LD_K_QKV, LD_K_ATTN, LD_K_WO, LD_K_W13, LD_K_W2, LD_K_CLS = range(6)
 
 # every entry point declared in include/ld.h
 EXPORTS = [
-    "ld_arena_bytes", "ld_model_init", "ld_prefill", "ld_decode_step", "ld_kv_reset",
+    "ld_arena_bytes", "ld_model_init", "ld_prefill", "ld_decode_step", "ld_generate", "ld_kv_reset",
     "ld_set_pos", "ld_get_pos", "ld_read_weights", "ld_status", "ld_profile",
     "ld_profile_read", "ld_synth_prompt", "ld_model_free", "ld_strerror",
 ]
@@ -55,6 +55,7 @@ def lib():
         L.ld_model_init.argtypes = [C.POINTER(LdConfig), u64, vp, sz, vp, C.POINTER(vp)]
         L.ld_prefill.argtypes = [vp, i32, i32, C.POINTER(i32), vp, vp, i32]
         L.ld_decode_step.argtypes = [vp, i32, vp, i32, vp, vp]
+        L.ld_generate.argtypes = [vp, i32, i32, vp, i32, vp, vp]
         L.ld_kv_reset.argtypes = [vp]
         L.ld_set_pos.argtypes = [vp, i32]
         L.ld_get_pos.argtypes = [vp, C.POINTER(i32)]

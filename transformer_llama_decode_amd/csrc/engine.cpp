@@ -79,13 +79,14 @@ void make_layout(const ld_config* c, Layout* L) {
   L->att = take(R * d * 4);
   L->g = take(R * f * 4);
   L->attn_part = take((size_t)kMaxAttnParts * (hd + 2) * 8);
-  L->attn_ticket = take((size_t)kMaxAttnParts * 4);
   L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
   L->arg_val = take(L->arg_parts * 4);
   L->arg_idx = take(L->arg_parts * 4);
   L->tok = take(R * 4);
   L->next = take(R * 4);
   L->err = take(4);
+  L->pos_dev = take(2 * 4);
+  L->gen = take(S * B * 4);
   L->total = off;
 }
 
@@ -111,6 +112,12 @@ struct ld_model {
   bool tok_ev_live[kTokSlots];
   int tok_slot;
   Prof prof[LD_K_COUNT];
+  // on-device generation loop: one decode step captured as a HIP graph
+  bool dev_pos;            // launches read the position from device memory (while capturing)
+  hipStream_t cap_stream;  // private stream the step is captured on
+  hipGraphExec_t gexec;    // replayable step, for (g_batch, g_logits)
+  int g_batch;
+  float* g_logits;
 
   template <typename T>
   T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
@@ -137,7 +144,7 @@ struct ProfScope {
   bool in_dispatch;
   ProfScope(ld_model* m, int k, bool in_dispatch_ = false)
       : p(&m->prof[k]), s(m->stream), idx(-1), in_dispatch(in_dispatch_) {
-    if (p->on && p->used < kProfPairs) {
+    if (p->on && p->used < kProfPairs && !m->dev_pos) {
       idx = p->used++;
       if (!in_dispatch) (void)hipEventRecord(p->ev[2 * idx], s);
     }
@@ -273,7 +280,7 @@ struct Uploader {
   }
 };
 
-int enqueue_host_tokens(ld_model* m, const int32_t* host, size_t n) {
+int enqueue_host_tokens(ld_model* m, const int32_t* host, size_t n, int* dst) {
   const int slot = m->tok_slot;
   m->tok_slot = (m->tok_slot + 1) % kTokSlots;
   if (m->tok_ev_live[slot]) {
@@ -281,8 +288,8 @@ int enqueue_host_tokens(ld_model* m, const int32_t* host, size_t n) {
     m->tok_ev_live[slot] = false;
   }
   std::memcpy(m->tok_host[slot], host, n * sizeof(int32_t));
-  LD_TRY_HIP(hipMemcpyAsync(m->at<int>(m->lay.tok), m->tok_host[slot], n * sizeof(int32_t),
-                            hipMemcpyHostToDevice, m->stream));
+  LD_TRY_HIP(hipMemcpyAsync(dst, m->tok_host[slot], n * sizeof(int32_t), hipMemcpyHostToDevice,
+                            m->stream));
   LD_TRY_HIP(hipEventRecord(m->tok_ev[slot], m->stream));
   m->tok_ev_live[slot] = true;
   return LD_OK;
@@ -293,6 +300,7 @@ int enqueue_host_tokens(ld_model* m, const int32_t* host, size_t n) {
 // Batch-1 layers on the GEMV path at position `pos`: the token's embedding is already in x.
 int layers_gemv(ld_model* m, int pos) {
   const ld_config& c = m->c;
+  const int* pos_dev = m->dev_pos ? m->at<int>(m->lay.pos_dev) : nullptr;
   const int d = c.dim, f = c.hidden_dim;
   float* x = m->at<float>(m->lay.x);
   float* q = m->at<float>(m->lay.q);
@@ -307,16 +315,15 @@ int layers_gemv(ld_model* m, int pos) {
       a.W = m->layer(l, m->lay.o_wqkv); a.N = 3 * d; a.K = d; a.stream = m->stream_weights;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
-      a.pos = pos; a.d = d; a.hd = m->hd; a.seq_pad = m->lay.seq_pad;
+      a.pos = pos; a.d = d; a.hd = m->hd; a.seq_pad = m->lay.seq_pad; a.pos_dev = pos_dev;
       LD_TRY_HIP(launch_gemv_qkv(a, m->stream));
     }
     {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
-      a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
-      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
@@ -351,6 +358,7 @@ int layers_gemv(ld_model* m, int pos) {
 // rows = B * n_tok rows (sequence-major) on the MFMA GEMM path.
 int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
   const ld_config& c = m->c;
+  const int* pos_dev = m->dev_pos ? m->at<int>(m->lay.pos_dev) : nullptr;
   const int d = c.dim, f = c.hidden_dim;
   float* x = m->at<float>(m->lay.x);
   float* xn = m->at<float>(m->lay.xn);
@@ -368,16 +376,15 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
       a.pos = pos; a.n_tok = n_tok; a.d = d; a.hd = m->hd; a.H = c.n_heads;
-      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
       LD_TRY_HIP(launch_gemm_qkv(a, m->stream));
     }
     {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
-      a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
-      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
@@ -457,8 +464,57 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
   // arg-max of each sequence's last row (every row is a last row unless all_pos)
   const int stride = (all_pos && cls_rows > 1) ? n_tok : 1;
   const int offset = (all_pos && cls_rows > 1) ? n_tok - 1 : 0;
-  LD_TRY_HIP(launch_argmax_finalize(pv, pi, B, nparts, stride, offset, next, next_int, m->stream));
+  FinalizeRing ring{nullptr, nullptr, nullptr};
+  if (m->dev_pos) {
+    int* pd = m->at<int>(m->lay.pos_dev);
+    ring = FinalizeRing{m->at<int>(m->lay.gen), pd, pd + 1};
+  }
+  LD_TRY_HIP(launch_argmax_finalize(pv, pi, B, nparts, stride, offset, next, next_int,
+                                    m->dev_pos ? &ring : nullptr, m->stream));
   return LD_OK;
+}
+
+// Capture one decode step of `batch` rows as a HIP graph that reads its
+// position and input tokens from device memory: the embedding kernel takes the
+// position pair's pending value, the arg-max kernel writes the next tokens
+// back as the following step's input, appends them to the token ring and
+// advances the pending position.  Replaying the graph n times decodes n
+// positions with no host work per step.
+int build_step_graph(ld_model* m, int batch, float* dev_logits) {
+  if (m->gexec != nullptr && m->g_batch == batch && m->g_logits == dev_logits) return LD_OK;
+  if (m->gexec != nullptr) {
+    LD_TRY_HIP(hipGraphExecDestroy(m->gexec));
+    m->gexec = nullptr;
+  }
+  const ld_config& c = m->c;
+  hipStream_t user = m->stream;
+  m->stream = m->cap_stream;
+  m->dev_pos = true;
+  hipGraph_t g = nullptr;
+  int rc = LD_OK;
+  if (hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    rc = LD_E_HIP;
+  } else {
+    int* pd = m->at<int>(m->lay.pos_dev);
+    if (launch_embed(m->at<int>(m->lay.next), m->at<float>(m->lay.E), m->at<float>(m->lay.x), batch,
+                     c.dim, c.vocab_size, m->at<int>(m->lay.err), pd + 1, pd, m->stream) != hipSuccess)
+      rc = LD_E_HIP;
+    if (rc == LD_OK) rc = (batch == 1) ? layers_gemv(m, 0) : layers_gemm(m, batch, 1, 0);
+    if (rc == LD_OK) rc = head(m, batch, 1, false, dev_logits, 1, 0, nullptr);
+    if (hipStreamEndCapture(m->cap_stream, &g) != hipSuccess && rc == LD_OK) rc = LD_E_HIP;
+  }
+  m->dev_pos = false;
+  m->stream = user;
+  if (rc == LD_OK && hipGraphInstantiate(&m->gexec, g, nullptr, nullptr, 0) != hipSuccess) {
+    m->gexec = nullptr;
+    rc = LD_E_HIP;
+  }
+  if (g != nullptr) (void)hipGraphDestroy(g);
+  if (rc == LD_OK) {
+    m->g_batch = batch;
+    m->g_logits = dev_logits;
+  }
+  return rc;
 }
 
 bool tokens_valid(const int32_t* t, size_t n, int V) {
@@ -509,6 +565,11 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
     m->stream_weights = wbytes > ((size_t)256 << 20);
   }
   m->tok_slot = 0;
+  m->dev_pos = false;
+  m->cap_stream = nullptr;
+  m->gexec = nullptr;
+  m->g_batch = 0;
+  m->g_logits = nullptr;
   if (hipGetDevice(&m->device) != hipSuccess) {
     delete m;
     return LD_E_HIP;
@@ -521,6 +582,10 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
     ld_model_free(m);
     return code;
   };
+  if (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess) {
+    m->cap_stream = nullptr;
+    return fail(LD_E_HIP);
+  }
   for (int i = 0; i < kTokSlots; ++i) {
     if (hipHostMalloc((void**)&m->tok_host[i], sizeof(int32_t) * L.rows, hipHostMallocDefault) !=
             hipSuccess ||
@@ -570,7 +635,6 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
         hipMemsetAsync(m->arena + L.Kc, 0, L.Vc - L.Kc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.Vc, 0, L.x - L.Vc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.err, 0, 4, m->stream) != hipSuccess ||
-        hipMemsetAsync(m->arena + L.attn_ticket, 0, (size_t)kMaxAttnParts * 4, m->stream) != hipSuccess ||
         hipStreamSynchronize(m->stream) != hipSuccess)
       return fail(LD_E_HIP);
   }
@@ -586,12 +650,12 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
   DeviceGuard dg(m->device);
   const int* d_tok = tokens_on_device ? tokens : m->at<int>(m->lay.tok);
   if (!tokens_on_device) {
-    int rc = enqueue_host_tokens(m, tokens, (size_t)batch);
+    int rc = enqueue_host_tokens(m, tokens, (size_t)batch, m->at<int>(m->lay.tok));
     if (rc != LD_OK) return rc;
   }
   const ld_config& c = m->c;
   LD_TRY_HIP(launch_embed(d_tok, m->at<float>(m->lay.E), m->at<float>(m->lay.x), batch, c.dim,
-                          c.vocab_size, m->at<int>(m->lay.err), m->stream));
+                          c.vocab_size, m->at<int>(m->lay.err), nullptr, nullptr, m->stream));
   int rc = (batch == 1) ? layers_gemv(m, m->pos) : layers_gemm(m, batch, 1, m->pos);
   if (rc != LD_OK) return rc;
   rc = head(m, batch, 1, false, dev_logits, 1, 0, dev_next);
@@ -618,10 +682,11 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
     for (int b = 0; b < batch; ++b)
       std::memcpy(&chunk_tok[(size_t)b * nc], host_tokens + (size_t)b * n_tokens + t0,
                   sizeof(int32_t) * nc);
-    int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows);
+    int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows, m->at<int>(m->lay.tok));
     if (rc != LD_OK) return rc;
     LD_TRY_HIP(launch_embed(m->at<int>(m->lay.tok), m->at<float>(m->lay.E), m->at<float>(m->lay.x),
-                            rows, c.dim, c.vocab_size, m->at<int>(m->lay.err), m->stream));
+                            rows, c.dim, c.vocab_size, m->at<int>(m->lay.err), nullptr, nullptr,
+                            m->stream));
     rc = (rows == 1) ? layers_gemv(m, pos0 + t0) : layers_gemm(m, rows, nc, pos0 + t0);
     if (rc != LD_OK) return rc;
     const bool last = t0 + nc >= n_tokens;
@@ -632,6 +697,33 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
     }
   }
   m->pos = pos0 + n_tokens;
+  return LD_OK;
+}
+
+int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* tokens,
+                int32_t tokens_on_device, float* dev_logits, int32_t* dev_out) {
+  if (!m || !tokens || batch <= 0 || batch > m->c.max_batch || n_steps < 0) return LD_E_INVAL;
+  if ((int64_t)m->pos + n_steps > m->c.max_seq) return LD_E_RANGE;
+  if (!tokens_on_device && !tokens_valid(tokens, (size_t)batch, m->c.vocab_size)) return LD_E_INVAL;
+  if (n_steps == 0) return LD_OK;
+  DeviceGuard dg(m->device);
+  int rc = build_step_graph(m, batch, dev_logits);
+  if (rc != LD_OK) return rc;
+  int* first = m->at<int>(m->lay.next);   // the graph's input tokens
+  if (tokens_on_device) {
+    LD_TRY_HIP(hipMemcpyAsync(first, tokens, sizeof(int32_t) * batch, hipMemcpyDeviceToDevice,
+                              m->stream));
+  } else {
+    rc = enqueue_host_tokens(m, tokens, (size_t)batch, first);
+    if (rc != LD_OK) return rc;
+  }
+  LD_TRY_HIP(launch_set_int(m->at<int>(m->lay.pos_dev) + 1, m->pos, m->stream));
+  for (int i = 0; i < n_steps; ++i) LD_TRY_HIP(hipGraphLaunch(m->gexec, m->stream));
+  if (dev_out != nullptr)
+    LD_TRY_HIP(hipMemcpyAsync(dev_out, m->at<int>(m->lay.gen) + (size_t)m->pos * batch,
+                              sizeof(int32_t) * (size_t)n_steps * batch, hipMemcpyDeviceToDevice,
+                              m->stream));
+  m->pos += n_steps;
   return LD_OK;
 }
 
@@ -764,6 +856,8 @@ void ld_model_free(ld_model* m) {
   }
   for (auto& p : m->prof)
     for (auto& e : p.ev) hipEventDestroy(e);
+  if (m->gexec) hipGraphExecDestroy(m->gexec);
+  if (m->cap_stream) hipStreamDestroy(m->cap_stream);
   delete m;
 }
 

@@ -14,10 +14,15 @@
 //    dimensions; the four partial outputs are summed in LDS at the end;
 //  * all arithmetic after the fp32 loads is fp64 (scores, exp, sums, weighted
 //    sum), rounded once when the output is stored.
-// When few (row, head) pairs exist (batch-1 decode) each tile gets its own
-// workgroup so one token's attention is spread over the GPU (flash-decoding
-// style); the per-tile (o, m, l) partials are merged by the last workgroup of
-// each (row, head) to finish, found with an atomic ticket -- no second launch.
+// When few (row, head) pairs exist (batch-1 decode) the tiles of a head are
+// split over several workgroups so one token's attention is spread over the GPU
+// (flash-decoding style); a second launch merges the per-chunk (o, m, l)
+// partials.  (Merging inside the first launch, by the last workgroup of each
+// head to finish, needs device-scope release/acquire fences that measured
+// slower on MI355X than the extra launch.)
+// The position may come from device memory (graph replays of the decode step):
+// then the chunk count is fixed by the cache length and each workgroup derives
+// its tile range from the position it reads.
 #include "dev_common.hpp"
 #include "ld_internal.hpp"
 
@@ -29,37 +34,28 @@ constexpr int kThreads = 256;
 constexpr int kTile = 64;
 constexpr int kMaxHd = 256;
 constexpr int kSplitBelow = 512;   // split heads over tiles when rows*heads is below this
-constexpr bool kFusedMerge = false;   // measured: agent-scope fences cost more than a merge launch
 
 // Merge the chunk partials (o_c, m_c, l_c) of one (row, head) into the output:
-// o = sum_c o_c e^(m_c - m) / sum_c l_c e^(m_c - m), m = max_c m_c.  One workgroup.
-__device__ void merge_unit(const AttnArgs& a, int r, int h, int nchunk) {
-  __shared__ double wc[kMaxAttnParts];
-  __shared__ double l_tot;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hd = a.hd;
+// o = sum_c o_c e^(m_c - m) / sum_c l_c e^(m_c - m), m = max_c m_c.  Thread i
+// finishes dimension i; every load's address is known up front, so all of
+// them are in flight together (one memory round trip).
+__global__ void __launch_bounds__(kThreads) k_attn_merge(AttnArgs a, int nchunk) {
+  const int r = blockIdx.y, h = blockIdx.x, i = threadIdx.x, hd = a.hd;
+  if (i >= hd) return;
   const double* pu = a.part + ((size_t)r * a.H + h) * nchunk * (hd + 2);
-  if (w == 0) {
-    double m = -INFINITY;
-    for (int cc = lane; cc < nchunk; cc += kWave) m = fmax(m, pu[(size_t)cc * (hd + 2) + hd]);
-    m = wave_max(m);
-    double l = 0.0;
-    for (int cc = lane; cc < nchunk; cc += kWave) {
-      const double* pc = pu + (size_t)cc * (hd + 2);
-      const double wgt = pc[hd + 1] > 0.0 ? exp(pc[hd] - m) : 0.0;   // empty chunks weigh 0
-      wc[cc] = wgt;
-      l = fma(pc[hd + 1], wgt, l);
-    }
-    l = wave_sum(l);
-    if (lane == 0) l_tot = l;
+  double m = -INFINITY;
+#pragma unroll 8
+  for (int c = 0; c < nchunk; ++c) m = fmax(m, pu[(size_t)c * (hd + 2) + hd]);
+  double l = 0.0, acc = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < nchunk; ++c) {
+    const double* pc = pu + (size_t)c * (hd + 2);
+    const double lc = pc[hd + 1];
+    const double wgt = lc > 0.0 ? exp(pc[hd] - m) : 0.0;   // empty chunks (o = 0, l = 0) weigh 0
+    l = fma(lc, wgt, l);
+    acc = fma(pc[i], wgt, acc);
   }
-  __syncthreads();
-  float* out = a.out + (size_t)r * a.d + (size_t)h * hd;
-  for (int i = threadIdx.x; i < hd; i += kThreads) {
-    double acc = 0.0;
-    for (int cc = 0; cc < nchunk; ++cc)
-      if (wc[cc] != 0.0) acc = fma(pu[(size_t)cc * (hd + 2) + i], wc[cc], acc);
-    out[i] = (float)(acc / l_tot);
-  }
+  a.out[(size_t)r * a.d + (size_t)h * hd + i] = (float)(acc / l);
 }
 
 // K and V of one 64-position tile as one wave loads them: head dimensions
@@ -72,18 +68,18 @@ struct TileRegs {
   float v[16][DPL];
 };
 
+// Loads the whole tile (every tile index below Sp/64 lies inside the cache);
+// rows past the history are zeroed afterwards by mask_tile.
 template <int HD>
 __device__ __forceinline__ void load_tile(TileRegs<HD>& t, const float4* kt, const float* vb, int tile,
-                                          int kvlen, int w, int lane) {
+                                          int w, int lane) {
   constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
   const int j0 = tile * kTile;
   const float4* kp = kt + ((size_t)tile * (HD / 4) + w * KQ) * kTile + lane;
 #pragma unroll
   for (int i = 0; i < KQ; ++i) t.k[i] = kp[i * kTile];
-  const int vrows = kvlen - (j0 + 16 * w);   // rows of this wave inside the history (may be <= 0)
   const float* vp = vb + (size_t)(j0 + 16 * w) * HD + lane * DPL;
-  const bool lane_in = lane * DPL < HD;
-  if (vrows >= 16 && lane_in) {              // the common case: the whole slice is history
+  if (lane * DPL < HD) {
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       if (DPL == 2) {
@@ -99,27 +95,42 @@ __device__ __forceinline__ void load_tile(TileRegs<HD>& t, const float4* kt, con
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj)
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) t.v[jj][k] = (jj < vrows && lane_in) ? vp[jj * HD + k] : 0.f;
+      for (int k = 0; k < DPL; ++k) t.v[jj][k] = 0.f;
   }
 }
 
-template <int HD, bool FUSED>   // HD: head dimension (a multiple of 16, <= 256); FUSED: the
-// last chunk to finish merges (atomic ticket), else a separate merge launch
-__global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int tiles_per_chunk) {
+// Zero the value rows at or past the history length: their weights are 0, and
+// a stale cache row must not turn 0 * value into a NaN.
+template <int HD>
+__device__ __forceinline__ void mask_tile(TileRegs<HD>& t, int tile, int kvlen, int w) {
+  constexpr int DPL = TileRegs<HD>::DPL;
+  const int vrows = kvlen - (tile * kTile + 16 * w);   // rows of this wave inside the history
+  if (vrows >= 16) return;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) t.v[jj][k] = jj < vrows ? t.v[jj][k] : 0.f;
+}
+
+// HD: head dimension (a multiple of 16, <= 256).  Workgroup (c, h, r) takes
+// chunk c of nchunk equal runs of the row's 64-position tiles.
+template <int HD>
+__global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
   constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
   constexpr int hd = HD;
   __shared__ float4 qs4[kMaxHd / 4];
   __shared__ double sp[4][kTile];
   __shared__ double es[kTile];
   __shared__ double ow[4][kMaxHd];
-  __shared__ int is_last;
   const int c = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = r / a.n_tok, t = r - b * a.n_tok;
-  const int kvlen = a.pos + t + 1;
+  const int pos = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
+  const int kvlen = pos + t + 1;
   const int ntiles = (kvlen + kTile - 1) / kTile;
-  const int tile0 = c * tiles_per_chunk;
-  const int tile1 = min(tile0 + tiles_per_chunk, ntiles);
+  const int per = (ntiles + nchunk - 1) / nchunk;
+  const int tile0 = c * per;
+  const int tile1 = min(tile0 + per, ntiles);
 
   const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * HD;
   const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);   // [Sp/64][HD/4][64] float4
@@ -127,7 +138,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int t
   const double sqrt_hd = sqrt((double)HD);
 
   TileRegs<HD> cur;
-  if (tile0 < tile1) load_tile<HD>(cur, kt, vb, tile0, kvlen, w, lane);   // first tile in flight
+  if (tile0 < tile1) load_tile<HD>(cur, kt, vb, tile0, w, lane);   // first tile in flight
   const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
   for (int i = threadIdx.x; i < HD / 4; i += kThreads) qs4[i] = q4[i];
   __syncthreads();
@@ -139,6 +150,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int t
 
   for (int tile = tile0; tile < tile1; ++tile) {
     const int j0 = tile * kTile;
+    mask_tile<HD>(cur, tile, kvlen, w);
     // ---- partial scores over this wave's dimensions (4 independent chains)
     double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -177,7 +189,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int t
     for (int k = 0; k < DPL; ++k) o[k] = oo[k][0] + oo[k][1];
     m_run = m_new;
     if (tile + 1 < tile1) {
-      load_tile<HD>(cur, kt, vb, tile + 1, kvlen, w, lane);
+      load_tile<HD>(cur, kt, vb, tile + 1, w, lane);
       __syncthreads();   // sp / es are rewritten by the next tile
     }
   }
@@ -212,42 +224,32 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk, int t
       part[hd] = m_run;
       part[hd + 1] = l_run;
     }
-    if (FUSED) __threadfence();   // release: the partial is visible device-wide before the ticket
   }
-  if (!FUSED) return;             // a separate merge launch follows
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    is_last = atomicAdd(&a.ticket[unit], 1) == nchunk - 1;
-    if (is_last) __threadfence();   // acquire: see every other chunk's partial
-  }
-  __syncthreads();
-  if (!is_last) return;
-  merge_unit(a, r, h, nchunk);
-  if (threadIdx.x == 0) a.ticket[unit] = 0;   // ready for the next launch
-}
-
-__global__ void __launch_bounds__(kThreads) k_attn_merge(AttnArgs a, int nchunk) {
-  merge_unit(a, blockIdx.y, blockIdx.x, nchunk);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  const int maxkv = a.pos + a.n_tok;              // longest history among the rows
-  const int tiles = (maxkv + kTile - 1) / kTile;
   const int units = a.rows * a.H;
-  int per = tiles;                                // tiles per chunk
+  int nchunk = 1;
   if (units < kSplitBelow) {
-    // about 256 workgroups: one or two tiles each (measured best at the 7B decode shape)
-    per = (units * tiles) / 256;
-    if (per < 1) per = 1;
-    while ((size_t)units * ((tiles + per - 1) / per) > (size_t)kMaxAttnParts) ++per;
+    if (a.pos_dev != nullptr) {
+      // position unknown on the host: a fixed split, about 512 workgroups, at
+      // most one chunk per tile of the cache
+      nchunk = std::max(1, std::min(a.seq_pad / kTile, 512 / units));
+    } else {
+      // about 256 workgroups: one or two tiles each (measured best at the 7B decode shape)
+      const int tiles = (a.pos + a.n_tok + kTile - 1) / kTile;   // longest history among the rows
+      int per = std::max(1, (units * tiles) / 256);
+      while ((size_t)units * ((tiles + per - 1) / per) > (size_t)kMaxAttnParts) ++per;
+      nchunk = (tiles + per - 1) / per;
+    }
+    while (nchunk > 1 && (size_t)units * nchunk > (size_t)kMaxAttnParts) --nchunk;
   }
-  const int nchunk = (tiles + per - 1) / per;
   dim3 grid(nchunk, a.H, a.rows);
   switch (a.hd) {
 #define LD_ATTN_CASE(HD) \
-    case HD: hipLaunchKernelGGL((k_attn<HD, kFusedMerge>), grid, dim3(kThreads), 0, s, a, nchunk, per); break;
+    case HD: hipLaunchKernelGGL((k_attn<HD>), grid, dim3(kThreads), 0, s, a, nchunk); break;
     LD_ATTN_CASE(16) LD_ATTN_CASE(32) LD_ATTN_CASE(48) LD_ATTN_CASE(64) LD_ATTN_CASE(80) LD_ATTN_CASE(96)
     LD_ATTN_CASE(112) LD_ATTN_CASE(128) LD_ATTN_CASE(144) LD_ATTN_CASE(160) LD_ATTN_CASE(176)
     LD_ATTN_CASE(192) LD_ATTN_CASE(208) LD_ATTN_CASE(224) LD_ATTN_CASE(240) LD_ATTN_CASE(256)
@@ -255,7 +257,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nchunk == 1 || kFusedMerge) return e;
+  if (e != hipSuccess || nchunk == 1) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.rows), dim3(kThreads), 0, s, a, nchunk);
   return hipGetLastError();
 }

@@ -158,6 +158,7 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
         }
   } else if (EPI == EPI_QKV) {
     const int d = a.d, hd = a.hd, half = hd >> 1;
+    const int pos0 = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -171,7 +172,7 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           const bool odd = col & 1;
           float y0 = odd ? partner : v, y1 = odd ? v : partner;
           const int sec = col / d, c = col - sec * d, h = c / hd, ii = c - h * hd;
-          const int b = row / a.n_tok, p = a.pos + (row - b * a.n_tok);
+          const int b = row / a.n_tok, p = pos0 + (row - b * a.n_tok);
           if (sec < 2) {
             const int t = p * half + (ii >> 1);
             rope_pair(y0, y1, a.rcos[t], a.rsin[t], y0, y1);
@@ -338,12 +339,13 @@ __global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
     }
   } else if (EPI == EPI_QKV) {
     const int d = a.d, hd = a.hd, half = hd >> 1;
+    const int pos0 = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
     for (int e = tid; e < 32 * 32; e += blockDim.x) {
       const int rl = e >> 5, cl = 2 * (e & 31), r = m0 + rl, col = n0 + cl;
       if (r >= M || col >= N) continue;
       float y0 = tile(rl, cl), y1 = tile(rl, cl + 1);
       const int sec = col / d, c = col - sec * d, h = c / hd, ii = c - h * hd;
-      const int b = r / a.n_tok, p = a.pos + (r - b * a.n_tok);
+      const int b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
       if (sec < 2) {
         const int t = p * half + (ii >> 1);
         rope_pair(y0, y1, a.rcos[t], a.rsin[t], y0, y1);

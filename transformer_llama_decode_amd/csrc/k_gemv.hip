@@ -186,11 +186,13 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   const bool pre = grp < ngroups && (K4 >> 6) >= U;
   if (pre) load_batch<NR, U, NT>(wpre, rows, 0, lane);
 
+  // position of the token (rotary angle, KV-cache slot)
+  const int pos = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
   if (EPI == EPI_QKV) {
     const int half = a.hd >> 1;
     for (int i = threadIdx.x; i < half; i += kThreads) {
-      rope_cs[i] = a.rcos[(size_t)a.pos * half + i];
-      rope_cs[128 + i] = a.rsin[(size_t)a.pos * half + i];
+      rope_cs[i] = a.rcos[(size_t)pos * half + i];
+      rope_cs[128 + i] = a.rsin[(size_t)pos * half + i];
     }
   }
   stage_input(xs, a.x, a.gain, K, a.eps, red);
@@ -243,10 +245,10 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         a.q_out[c + 1] = y1;
       } else if (sec == 1) {
         float* kh = a.kc + (size_t)h * a.seq_pad * hd;
-        kh[ktile_index(a.pos, ii, hd)] = y0;
-        kh[ktile_index(a.pos, ii + 1, hd)] = y1;
+        kh[ktile_index(pos, ii, hd)] = y0;
+        kh[ktile_index(pos, ii + 1, hd)] = y1;
       } else {
-        float* vrow = a.vc + ((size_t)h * a.seq_pad + a.pos) * hd;
+        float* vrow = a.vc + ((size_t)h * a.seq_pad + pos) * hd;
         vrow[ii] = y0;
         vrow[ii + 1] = y1;
       }

@@ -10,8 +10,9 @@ namespace {
 // x[r] = E[tok[r]]; an out-of-range id (only possible for ids read from device
 // memory) is replaced by 0 and flagged.
 __global__ void __launch_bounds__(256) k_embed(const int* tok, const float* E, float* x, int d, int V,
-                                               int* err) {
+                                               int* err, const int* pos_src, int* pos_dst) {
   const int r = blockIdx.x;
+  if (pos_dst != nullptr && r == 0 && threadIdx.x == 0) *pos_dst = *pos_src;
   int t = tok[r];
   if (t < 0 || t >= V) {
     if (threadIdx.x == 0) atomicOr(err, 2);
@@ -58,7 +59,7 @@ __global__ void __launch_bounds__(256) k_rmsnorm_rows(const float* in, float* ou
 // Output row r reads partial row r * row_stride + row_offset.
 __global__ void __launch_bounds__(256) k_argmax_finalize(const float* pv, const int* pi, int nparts,
                                                          int row_stride, int row_offset, int* next,
-                                                         int* next2) {
+                                                         int* next2, FinalizeRing ring) {
   __shared__ float sv[4];
   __shared__ int si[4];
   const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -77,6 +78,12 @@ __global__ void __launch_bounds__(256) k_argmax_finalize(const float* pv, const 
     if (bi == 0x7fffffff) bi = 0;   // every value was NaN: flagged by the producer
     if (next) next[r] = bi;
     if (next2) next2[r] = bi;
+    if (ring.ring != nullptr) {
+      // the token generated at position p (the step's input position)
+      const int p = *ring.pos_dev;
+      ring.ring[(size_t)p * gridDim.x + r] = bi;
+      if (r == 0) *ring.pos_next = p + 1;
+    }
   }
 }
 
@@ -86,11 +93,15 @@ __global__ void k_fill(float* p, float v, size_t n) {
     p[i] = v;
 }
 
+__global__ void k_set_int(int* p, int v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
 }  // namespace
 
 hipError_t launch_embed(const int* tok, const float* E, float* x, int rows, int d, int V, int* err,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err);
+                        const int* pos_src, int* pos_dst, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst);
   return hipGetLastError();
 }
 
@@ -103,9 +114,15 @@ hipError_t launch_rmsnorm_rows(const float* in, float* out, const float* gain, i
 
 hipError_t launch_argmax_finalize(const float* part_val, const int* part_idx, int rows, int nparts,
                                   int row_stride, int row_offset, int* next, int* next2,
-                                  hipStream_t s) {
+                                  const FinalizeRing* ring, hipStream_t s) {
+  const FinalizeRing rg = ring ? *ring : FinalizeRing{nullptr, nullptr, nullptr};
   hipLaunchKernelGGL(k_argmax_finalize, dim3(rows), dim3(256), 0, s, part_val, part_idx, nparts,
-                     row_stride, row_offset, next, next2);
+                     row_stride, row_offset, next, next2, rg);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_int(int* p, int v, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_int, dim3(1), dim3(64), 0, s, p, v);
   return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@
 //   V cache [L][Bmax][H][Sp][hd]  position-major rows
 //   activations for up to R rows: x, xn, q, att [R][d]; g [R][f]
 //   attention partials, arg-max partials, token buffers, error flag
+//   device position pair [pos, pos_next] and the generated-token ring
+//   [S][Bmax] of the on-device generation loop
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -40,7 +42,8 @@ enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS =
 struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
-  size_t x, xn, q, att, g, attn_part, attn_ticket, arg_val, arg_idx, tok, next, err;
+  size_t x, xn, q, att, g, attn_part, arg_val, arg_idx, tok, next, err;
+  size_t pos_dev, gen;
   size_t total;
   int rows;            // R: activation rows per forward pass
   int seq_pad;         // Sp
@@ -63,6 +66,7 @@ struct GemvArgs {
   const float* rcos;
   const float* rsin;
   int pos, d, hd, seq_pad;
+  const int* pos_dev;  // when set, the position is read from device memory instead of pos
   // residual epilogue
   float* resid;
   // SwiGLU epilogue
@@ -86,8 +90,9 @@ struct AttnArgs {
   const float* vc;     // V cache of this layer, sequence 0
   float* out;          // [rows][d]
   double* part;        // partial (o[hd], m, l) per (row, head, chunk)
-  int* ticket;         // per (row, head) arrival counters, zero between launches
   int rows, n_tok, pos, d, H, hd, seq_pad, bmax;
+  const int* pos_dev;  // when set, the position is read from device memory instead of pos,
+                       // and the chunk count is fixed by the cache length (graph replays)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
@@ -104,6 +109,7 @@ struct GemmArgs {
   const float* rcos;
   const float* rsin;
   int pos, n_tok, d, hd, H, seq_pad, bmax;
+  const int* pos_dev;  // when set, the position is read from device memory instead of pos
   // residual
   float* resid;
   // SwiGLU
@@ -122,15 +128,23 @@ hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_cls(const GemmArgs& a, int* nparts, hipStream_t s);
 
+// pos_dst/pos_src (both or neither): the first workgroup also copies *pos_src to *pos_dst
 hipError_t launch_embed(const int* tok, const float* E, float* x, int rows, int d, int V, int* err,
-                        hipStream_t s);
+                        const int* pos_src, int* pos_dst, hipStream_t s);
 // out row i <- rmsnorm(in row i * in_stride + in_offset)
 hipError_t launch_rmsnorm_rows(const float* in, float* out, const float* gain, int rows, int d,
                                int in_stride, int in_offset, double eps, hipStream_t s);
-// next[r] (and next2[r]) = arg-max of partial row r * row_stride + row_offset
+// next[r] (and next2[r]) = arg-max of partial row r * row_stride + row_offset.
+// With a ring: ring[p * rows + r] = the same token, p = *pos_dev, and *pos_next = p + 1.
+struct FinalizeRing {
+  int* ring;
+  const int* pos_dev;
+  int* pos_next;
+};
 hipError_t launch_argmax_finalize(const float* part_val, const int* part_idx, int rows, int nparts,
                                   int row_stride, int row_offset, int* next, int* next2,
-                                  hipStream_t s);
+                                  const FinalizeRing* ring, hipStream_t s);
+hipError_t launch_set_int(int* p, int v, hipStream_t s);
 hipError_t launch_fill(float* p, float v, size_t n, hipStream_t s);
 
 }  // namespace ld

@@ -83,6 +83,33 @@ class LlamaDecoder:
                                     nxt.data_ptr()), "ld_decode_step")
         return nxt
 
+    def generate(self, tokens, n_steps, logits=None, out=None):
+        """Greedy on-device generation of n_steps positions (one HIP graph replay each).
+
+        tokens: the first input ids, int32 host array [batch] or device tensor [batch].
+        Returns the int32 device tensor [n_steps, batch] of generated tokens (`out` if given).
+        """
+        torch = self.torch
+        if isinstance(tokens, torch.Tensor) and tokens.is_cuda:
+            assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+            B, ptr, on_dev = tokens.numel(), tokens.data_ptr(), 1
+            keep = None
+        else:
+            keep = np.ascontiguousarray(np.atleast_1d(tokens), dtype=np.int32)
+            B, ptr, on_dev = keep.size, keep.ctypes.data, 0
+        if out is None:
+            out = torch.empty((max(n_steps, 0), B), dtype=torch.int32, device=self.device)
+        assert out.dtype == torch.int32 and out.is_contiguous() and out.numel() >= n_steps * B
+        check(self.L.ld_generate(self._h, B, n_steps, ptr, on_dev,
+                                 logits.data_ptr() if logits is not None else None,
+                                 out.data_ptr()), "ld_generate")
+        return out
+
+    def generate_rc(self, tokens, n_steps):
+        """Like generate (host tokens, no outputs) but returns the status code."""
+        keep = np.ascontiguousarray(np.atleast_1d(tokens), dtype=np.int32)
+        return self.L.ld_generate(self._h, keep.size, n_steps, keep.ctypes.data, 0, None, None)
+
     def decode_step_rc(self, tokens, logits=None, next_out=None):
         """Like decode_step but returns the status code instead of raising."""
         keep = np.ascontiguousarray(np.atleast_1d(tokens), dtype=np.int32)

@@ -257,3 +257,4 @@ def test_out_of_range_device_token_is_reported(dev):
     assert gm.status() == LD_E_NONFINITE
     assert gm.status() == 0          # cleared after reporting
     gm.close()
+

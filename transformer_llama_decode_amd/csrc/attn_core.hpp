@@ -1,0 +1,185 @@
+// attn_core.hpp -- one workgroup's share of causal attention over the KV cache
+// (shared by the attention kernel and the fused attention + output projection).
+//
+// A workgroup of 4 waves takes one (row, head, chunk) unit: chunk c of nchunk
+// owns the row's 64-position tiles c, c + nchunk, c + 2 nchunk, ... (online
+// softmax partials need no contiguity).  For each tile all four waves first
+// issue every load of the tile at once -- wave w fetches head dimensions
+// [w*hd/4, (w+1)*hd/4) of the tile's 64 keys (K tiles are [hd/4][64][4], so each
+// load is a float4 per lane, 1 KiB per wave) and the 16 value rows of positions
+// [16w, 16w+16) -- so a tile costs about one HBM round trip.  Then:
+//  * scores: each wave's partial dot products over its dimensions meet in LDS
+//    and are summed in a fixed order (lane j = position j of the tile);
+//  * online softmax per wave with wave-level max/sum butterflies: every wave
+//    derives the same running max m and sum l from the same scores;
+//  * weighted values: wave w accumulates its 16 positions; lanes own head
+//    dimensions;
+//  * all arithmetic after the fp32 loads is fp64 (scores, exp, sums, weighted
+//    sum).
+// A chunk's first tile is c whatever the position, so when the position sits in
+// device memory (graph replays) the first tile's loads are issued before it
+// arrives.
+#pragma once
+
+#include "dev_common.hpp"
+#include "ld_internal.hpp"
+
+namespace ld {
+namespace attn {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;
+constexpr int kMaxHd = 256;
+
+// K and V of one 64-position tile as one wave loads them: head dimensions
+// [w*HD/4, (w+1)*HD/4) of the 64 keys, and the value rows of positions [16w, 16w+16)
+// (lane l holds dimensions l*DPL .. l*DPL+DPL-1 of each row).
+template <int HD>
+struct TileRegs {
+  static constexpr int KQ = HD / 16, DPL = (HD + 63) / 64;
+  float4 k[KQ];
+  float v[16][DPL];
+};
+
+// Loads the whole tile (every tile index below Sp/64 lies inside the cache);
+// rows past the history are zeroed afterwards by mask_tile.
+template <int HD>
+__device__ __forceinline__ void load_tile(TileRegs<HD>& t, const float4* kt, const float* vb, int tile,
+                                          int w, int lane) {
+  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
+  const int j0 = tile * kTile;
+  const float4* kp = kt + ((size_t)tile * (HD / 4) + w * KQ) * kTile + lane;
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) t.k[i] = kp[i * kTile];
+  const float* vp = vb + (size_t)(j0 + 16 * w) * HD + lane * DPL;
+  if (lane * DPL < HD) {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      if (DPL == 2) {
+        const float2 v2 = *reinterpret_cast<const float2*>(vp + jj * HD);
+        t.v[jj][0] = v2.x;
+        t.v[jj][DPL - 1] = v2.y;
+      } else {
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) t.v[jj][k] = vp[jj * HD + k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) t.v[jj][k] = 0.f;
+  }
+}
+
+// Zero the value rows at or past the history length: their weights are 0, and
+// a stale cache row must not turn 0 * value into a NaN.
+template <int HD>
+__device__ __forceinline__ void mask_tile(TileRegs<HD>& t, int tile, int kvlen, int w) {
+  constexpr int DPL = TileRegs<HD>::DPL;
+  const int vrows = kvlen - (tile * kTile + 16 * w);   // rows of this wave inside the history
+  if (vrows >= 16) return;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) t.v[jj][k] = jj < vrows ? t.v[jj][k] : 0.f;
+}
+
+// Unit (c, h, r) of nchunk chunks.  On return ow[w][i] holds wave w's share of
+// the unnormalised output sum_j e^(s_j - m) v_j[i] (sum the four in order 0..3),
+// m, l the running max and sum of the unit's scores (m = -inf, l = 0 and ow = 0
+// for a chunk with no tile) and ntiles the row's tile count (chunks c >= ntiles
+// have no tile).  Ends with a workgroup barrier.
+template <int HD>
+__device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r, int nchunk,
+                                          double (&ow)[4][kMaxHd], double& m_out, double& l_out,
+                                          int& ntiles_out) {
+  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
+  constexpr int hd = HD;
+  __shared__ float4 qs4[kMaxHd / 4];
+  __shared__ double sp[4][kTile];
+  __shared__ double es[kTile];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = r / a.n_tok, t = r - b * a.n_tok;
+  const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * HD;
+  const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);   // [Sp/64][HD/4][64] float4
+  const float* vb = a.vc + head_off;                                      // [Sp][HD]
+  const double sqrt_hd = sqrt((double)HD);
+
+  TileRegs<HD> cur;
+  // speculative first tile (c < nchunk <= Sp/64: inside the cache); unused if
+  // the history turns out shorter than c + 1 tiles
+  const bool spec = a.pos_dev != nullptr;
+  if (spec) load_tile<HD>(cur, kt, vb, c, w, lane);
+  const int pos = spec ? *a.pos_dev : a.pos;
+  const int kvlen = pos + t + 1;
+  const int ntiles = (kvlen + kTile - 1) / kTile;
+  if (!spec && c < ntiles) load_tile<HD>(cur, kt, vb, c, w, lane);   // first tile in flight
+  const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
+  for (int i = threadIdx.x; i < HD / 4; i += kThreads) qs4[i] = q4[i];
+  __syncthreads();
+
+  double m_run = -INFINITY, l_run = 0.0;
+  double o[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) o[k] = 0.0;
+
+  for (int tile = c; tile < ntiles; tile += nchunk) {
+    const int j0 = tile * kTile;
+    mask_tile<HD>(cur, tile, kvlen, w);
+    // ---- partial scores over this wave's dimensions (4 independent chains)
+    double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+      const float4 qv = qs4[w * KQ + i];
+      s4[0] = fma((double)qv.x, (double)cur.k[i].x, s4[0]);
+      s4[1] = fma((double)qv.y, (double)cur.k[i].y, s4[1]);
+      s4[2] = fma((double)qv.z, (double)cur.k[i].z, s4[2]);
+      s4[3] = fma((double)qv.w, (double)cur.k[i].w, s4[3]);
+    }
+    sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    __syncthreads();
+    // ---- online softmax (every wave derives the same m, l from the same scores)
+    const bool valid = j0 + lane < kvlen;
+    const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
+    const double m_new = fmax(m_run, wave_max(valid ? sc : -INFINITY));
+    const double scale = exp(m_run - m_new);   // 0 on the first tile (m_run = -inf)
+    const double e = valid ? exp(sc - m_new) : 0.0;
+    if (w == 0) es[lane] = e;
+    l_run = l_run * scale + wave_sum(e);
+    __syncthreads();
+    // ---- weighted values of this wave's 16 positions
+    double oo[DPL][2];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      oo[k][0] = o[k] * scale;
+      oo[k][1] = 0.0;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const double ej = es[16 * w + jj];   // 0 past the history
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) oo[k][jj & 1] = fma(ej, (double)cur.v[jj][k], oo[k][jj & 1]);
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = oo[k][0] + oo[k][1];
+    m_run = m_new;
+    if (tile + nchunk < ntiles) {
+      load_tile<HD>(cur, kt, vb, tile + nchunk, w, lane);
+      __syncthreads();   // sp / es are rewritten by the next tile
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    const int i = lane * DPL + k;
+    if (i < hd) ow[w][i] = o[k];
+  }
+  __syncthreads();
+  m_out = m_run;
+  l_out = l_run;
+  ntiles_out = ntiles;
+}
+
+}  // namespace attn
+}  // namespace ld

@@ -79,6 +79,7 @@ void make_layout(const ld_config* c, Layout* L) {
   L->att = take(R * d * 4);
   L->g = take(R * f * 4);
   L->attn_part = take((size_t)kMaxAttnParts * (hd + 2) * 8);
+  L->attn_ticket = take((size_t)kMaxAttnParts * 4);
   L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
   L->arg_val = take(L->arg_parts * 4);
   L->arg_idx = take(L->arg_parts * 4);
@@ -322,6 +323,7 @@ int layers_gemv(ld_model* m, int pos) {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
+      a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
       LD_TRY_HIP(launch_attention(a, m->stream));
@@ -383,6 +385,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
+      a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
       LD_TRY_HIP(launch_attention(a, m->stream));
@@ -635,6 +638,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
         hipMemsetAsync(m->arena + L.Kc, 0, L.Vc - L.Kc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.Vc, 0, L.x - L.Vc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.err, 0, 4, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.attn_ticket, 0, (size_t)kMaxAttnParts * 4, m->stream) != hipSuccess ||
         hipStreamSynchronize(m->stream) != hipSuccess)
       return fail(LD_E_HIP);
   }

@@ -1,230 +1,141 @@
-// k_attn.hip -- causal attention of query rows over the KV cache.
+// k_attn.hip -- causal attention of query rows over the KV cache (the unit of
+// work and its arithmetic are in attn_core.hpp).
 //
-// One workgroup (4 waves) takes one (row, head, chunk of 64-position tiles).
-// For each tile all four waves first issue every load of the tile at once --
-// wave w fetches head dimensions [w*hd/4, (w+1)*hd/4) of the tile's 64 keys
-// (K tiles are [hd/4][64][4], so each load is a float4 per lane, 1 KiB per
-// wave) and the 16 value rows of positions [16w, 16w+16) -- so a tile costs
-// about one HBM round trip.  Then:
-//  * scores: each wave's partial dot products over its dimensions meet in LDS
-//    and are summed in a fixed order (lane j = position j of the tile);
-//  * online softmax per wave with wave-level max/sum butterflies: every wave
-//    derives the same running max m and sum l from the same scores;
-//  * weighted values: wave w accumulates its 16 positions; lanes own head
-//    dimensions; the four partial outputs are summed in LDS at the end;
-//  * all arithmetic after the fp32 loads is fp64 (scores, exp, sums, weighted
-//    sum), rounded once when the output is stored.
 // When few (row, head) pairs exist (batch-1 decode) the tiles of a head are
 // split over several workgroups so one token's attention is spread over the GPU
-// (flash-decoding style); a second launch merges the per-chunk (o, m, l)
-// partials.  (Merging inside the first launch, by the last workgroup of each
-// head to finish, needs device-scope release/acquire fences that measured
-// slower on MI355X than the extra launch.)
+// (flash-decoding style); the last workgroup of each (row, head) to finish
+// merges the per-chunk (o, m, l) partials, found with an atomic ticket, so no
+// second launch is needed.
 // The position may come from device memory (graph replays of the decode step):
 // then the chunk count is fixed by the cache length and each workgroup derives
-// its tile range from the position it reads.
-#include "dev_common.hpp"
-#include "ld_internal.hpp"
+// its tiles from the position it reads.
+#include "attn_core.hpp"
 
 namespace ld {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTile = 64;
-constexpr int kMaxHd = 256;
+using attn::kThreads;
+using attn::kTile;
+using attn::kMaxHd;
+
 constexpr int kSplitBelow = 512;   // split heads over tiles when rows*heads is below this
 
-// Merge the chunk partials (o_c, m_c, l_c) of one (row, head) into the output:
-// o = sum_c o_c e^(m_c - m) / sum_c l_c e^(m_c - m), m = max_c m_c.  Thread i
-// finishes dimension i; every load's address is known up front, so all of
-// them are in flight together (one memory round trip).
-__global__ void __launch_bounds__(kThreads) k_attn_merge(AttnArgs a, int nchunk) {
-  const int r = blockIdx.y, h = blockIdx.x, i = threadIdx.x, hd = a.hd;
-  if (i >= hd) return;
-  const double* pu = a.part + ((size_t)r * a.H + h) * nchunk * (hd + 2);
-  double m = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < nchunk; ++c) m = fmax(m, pu[(size_t)c * (hd + 2) + hd]);
-  double l = 0.0, acc = 0.0;
-#pragma unroll 8
-  for (int c = 0; c < nchunk; ++c) {
-    const double* pc = pu + (size_t)c * (hd + 2);
-    const double lc = pc[hd + 1];
-    const double wgt = lc > 0.0 ? exp(pc[hd] - m) : 0.0;   // empty chunks (o = 0, l = 0) weigh 0
-    l = fma(lc, wgt, l);
-    acc = fma(pc[i], wgt, acc);
-  }
-  a.out[(size_t)r * a.d + (size_t)h * hd + i] = (float)(acc / l);
+// Values that cross workgroups inside one launch (the chunk partials) are
+// written and read with relaxed device-scope atomics: those are coherent across
+// the XCDs' L2 caches without an L2-wide release/acquire fence.  A writer waits
+// for its stores to complete before taking the ticket that announces them.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// K and V of one 64-position tile as one wave loads them: head dimensions
-// [w*HD/4, (w+1)*HD/4) of the 64 keys, and the value rows of positions [16w, 16w+16)
-// (lane l holds dimensions l*DPL .. l*DPL+DPL-1 of each row).
-template <int HD>
-struct TileRegs {
-  static constexpr int KQ = HD / 16, DPL = (HD + 63) / 64;
-  float4 k[KQ];
-  float v[16][DPL];
-};
+constexpr int kMergeBatch = 16;   // chunk partials loaded at once per thread
 
-// Loads the whole tile (every tile index below Sp/64 lies inside the cache);
-// rows past the history are zeroed afterwards by mask_tile.
-template <int HD>
-__device__ __forceinline__ void load_tile(TileRegs<HD>& t, const float4* kt, const float* vb, int tile,
-                                          int w, int lane) {
-  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
-  const int j0 = tile * kTile;
-  const float4* kp = kt + ((size_t)tile * (HD / 4) + w * KQ) * kTile + lane;
+// Merge of one (row, head)'s chunk partials by the last of its workgroups:
+// o = sum_c o_c e^(m_c - m) / sum_c l_c e^(m_c - m), m = max_c m_c, summed over c
+// in order.  Thread i finishes dimension i; the loads of kMergeBatch chunks are
+// issued together (one memory round trip per batch).
+__device__ __forceinline__ void merge_unit(const double* pu, int nchunk, int hd, float* out) {
+  const int i = threadIdx.x;
+  if (i >= hd) return;
+  constexpr int MB = kMergeBatch;
+  double mc[MB], lc[MB], oc[MB];
 #pragma unroll
-  for (int i = 0; i < KQ; ++i) t.k[i] = kp[i * kTile];
-  const float* vp = vb + (size_t)(j0 + 16 * w) * HD + lane * DPL;
-  if (lane * DPL < HD) {
+  for (int u = 0; u < MB; ++u) {
+    const double* pc = pu + (size_t)u * (hd + 2);
+    const bool in = u < nchunk;
+    mc[u] = in ? ld_dev(pc + hd) : -INFINITY;
+    lc[u] = in ? ld_dev(pc + hd + 1) : 0.0;
+    oc[u] = in ? ld_dev(pc + i) : 0.0;
+  }
+  double m = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      if (DPL == 2) {
-        const float2 v2 = *reinterpret_cast<const float2*>(vp + jj * HD);
-        t.v[jj][0] = v2.x;
-        t.v[jj][DPL - 1] = v2.y;
-      } else {
+  for (int u = 0; u < MB; ++u) m = fmax(m, mc[u]);
+  for (int c0 = MB; c0 < nchunk; c0 += MB) {
+    double mm[MB];
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) t.v[jj][k] = vp[jj * HD + k];
+    for (int u = 0; u < MB; ++u) mm[u] = c0 + u < nchunk ? ld_dev(pu + (size_t)(c0 + u) * (hd + 2) + hd) : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) m = fmax(m, mm[u]);
+  }
+  double l = 0.0, acc = 0.0;
+  for (int c0 = 0; c0 < nchunk; c0 += MB) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const double* pc = pu + (size_t)(c0 + u) * (hd + 2);
+        const bool in = c0 + u < nchunk;
+        mc[u] = in ? ld_dev(pc + hd) : -INFINITY;
+        lc[u] = in ? ld_dev(pc + hd + 1) : 0.0;
+        oc[u] = in ? ld_dev(pc + i) : 0.0;
       }
     }
-  } else {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj)
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) t.v[jj][k] = 0.f;
+    for (int u = 0; u < MB; ++u) {
+      if (c0 + u < nchunk) {
+        const double wgt = lc[u] > 0.0 ? exp(mc[u] - m) : 0.0;   // empty chunks (o = 0, l = 0) weigh 0
+        l = fma(lc[u], wgt, l);
+        acc = fma(oc[u], wgt, acc);
+      }
+    }
   }
+  out[i] = (float)(acc / l);
 }
 
-// Zero the value rows at or past the history length: their weights are 0, and
-// a stale cache row must not turn 0 * value into a NaN.
-template <int HD>
-__device__ __forceinline__ void mask_tile(TileRegs<HD>& t, int tile, int kvlen, int w) {
-  constexpr int DPL = TileRegs<HD>::DPL;
-  const int vrows = kvlen - (tile * kTile + 16 * w);   // rows of this wave inside the history
-  if (vrows >= 16) return;
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj)
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) t.v[jj][k] = jj < vrows ? t.v[jj][k] : 0.f;
-}
-
-// HD: head dimension (a multiple of 16, <= 256).  Workgroup (c, h, r) takes
-// chunk c of nchunk equal runs of the row's 64-position tiles.
 template <int HD>
 __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
-  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
-  constexpr int hd = HD;
-  __shared__ float4 qs4[kMaxHd / 4];
-  __shared__ double sp[4][kTile];
-  __shared__ double es[kTile];
   __shared__ double ow[4][kMaxHd];
+  __shared__ int is_last;
   const int c = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = r / a.n_tok, t = r - b * a.n_tok;
-  const int pos = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
-  const int kvlen = pos + t + 1;
-  const int ntiles = (kvlen + kTile - 1) / kTile;
-  const int per = (ntiles + nchunk - 1) / nchunk;
-  const int tile0 = c * per;
-  const int tile1 = min(tile0 + per, ntiles);
-
-  const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * HD;
-  const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);   // [Sp/64][HD/4][64] float4
-  const float* vb = a.vc + head_off;                                      // [Sp][HD]
-  const double sqrt_hd = sqrt((double)HD);
-
-  TileRegs<HD> cur;
-  if (tile0 < tile1) load_tile<HD>(cur, kt, vb, tile0, w, lane);   // first tile in flight
-  const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
-  for (int i = threadIdx.x; i < HD / 4; i += kThreads) qs4[i] = q4[i];
-  __syncthreads();
-
-  double m_run = -INFINITY, l_run = 0.0;
-  double o[DPL];
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) o[k] = 0.0;
-
-  for (int tile = tile0; tile < tile1; ++tile) {
-    const int j0 = tile * kTile;
-    mask_tile<HD>(cur, tile, kvlen, w);
-    // ---- partial scores over this wave's dimensions (4 independent chains)
-    double s4[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int i = 0; i < KQ; ++i) {
-      const float4 qv = qs4[w * KQ + i];
-      s4[0] = fma((double)qv.x, (double)cur.k[i].x, s4[0]);
-      s4[1] = fma((double)qv.y, (double)cur.k[i].y, s4[1]);
-      s4[2] = fma((double)qv.z, (double)cur.k[i].z, s4[2]);
-      s4[3] = fma((double)qv.w, (double)cur.k[i].w, s4[3]);
-    }
-    sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    __syncthreads();
-    // ---- online softmax (every wave derives the same m, l from the same scores)
-    const bool valid = j0 + lane < kvlen;
-    const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
-    const double m_new = fmax(m_run, wave_max(valid ? sc : -INFINITY));
-    const double scale = exp(m_run - m_new);   // 0 on the first tile (m_run = -inf)
-    const double e = valid ? exp(sc - m_new) : 0.0;
-    if (w == 0) es[lane] = e;
-    l_run = l_run * scale + wave_sum(e);
-    __syncthreads();
-    // ---- weighted values of this wave's 16 positions
-    double oo[DPL][2];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      oo[k][0] = o[k] * scale;
-      oo[k][1] = 0.0;
-    }
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const double ej = es[16 * w + jj];   // 0 past the history
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) oo[k][jj & 1] = fma(ej, (double)cur.v[jj][k], oo[k][jj & 1]);
-    }
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = oo[k][0] + oo[k][1];
-    m_run = m_new;
-    if (tile + 1 < tile1) {
-      load_tile<HD>(cur, kt, vb, tile + 1, w, lane);
-      __syncthreads();   // sp / es are rewritten by the next tile
-    }
-  }
-
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) {
-    const int i = lane * DPL + k;
-    if (i < hd) ow[w][i] = o[k];
-  }
-  __syncthreads();
-  const size_t unit = (size_t)r * a.H + h;
-  if (nchunk == 1) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int DPL = attn::TileRegs<HD>::DPL;
+  double m_run, l_run;
+  int ntiles;
+  attn::attn_unit<HD>(a, c, h, r, nchunk, ow, m_run, l_run, ntiles);
+  // chunks c >= ntiles hold no tile: they take no part in the merge
+  const int nreal = min(nchunk, ntiles);
+  if (c >= nreal) return;
+  float* out = a.out + (size_t)r * a.d + (size_t)h * HD;
+  if (nreal == 1) {
     if (w == 0) {
-      float* out = a.out + (size_t)r * a.d + (size_t)h * hd;
 #pragma unroll
       for (int k = 0; k < DPL; ++k) {
         const int i = lane * DPL + k;
-        if (i < hd) out[i] = (float)((((ow[0][i] + ow[1][i]) + ow[2][i]) + ow[3][i]) / l_run);
+        if (i < HD) out[i] = (float)((((ow[0][i] + ow[1][i]) + ow[2][i]) + ow[3][i]) / l_run);
       }
     }
     return;
   }
-  // ---- split head: publish this chunk's partial
-  double* part = a.part + (unit * nchunk + c) * (hd + 2);
+  // split head: publish this chunk's partial (o, m, l), then take a ticket; the
+  // last of the nreal chunks of the (row, head) to arrive merges them
+  const size_t unit = (size_t)r * a.H + h;
+  double* pu = a.part + unit * nchunk * (HD + 2);
   if (w == 0) {
+    double* part = pu + (size_t)c * (HD + 2);
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
       const int i = lane * DPL + k;
-      if (i < hd) part[i] = ((ow[0][i] + ow[1][i]) + ow[2][i]) + ow[3][i];
+      if (i < HD) st_dev(part + i, ((ow[0][i] + ow[1][i]) + ow[2][i]) + ow[3][i]);
     }
     if (lane == 0) {
-      part[hd] = m_run;
-      part[hd + 1] = l_run;
+      st_dev(part + HD, m_run);
+      st_dev(part + HD + 1, l_run);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(a.ticket + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              nreal - 1;
+  __syncthreads();
+  if (!is_last) return;
+  merge_unit(pu, nreal, HD, out);
+  if (threadIdx.x == 0) st_dev(a.ticket + unit, 0);   // every chunk has arrived: re-arm
 }
 
 }  // namespace
@@ -256,9 +167,6 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 #undef LD_ATTN_CASE
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nchunk == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.rows), dim3(kThreads), 0, s, a, nchunk);
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = a.M, N = a.N, K = a.K;
+  // QKV epilogue position, read at the start so the load overlaps the main loop
+  const int pos0 = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
 
   float4 ra[AL], rb[BL];
   floatx16 acc[MT][NT];
@@ -158,7 +160,6 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
         }
   } else if (EPI == EPI_QKV) {
     const int d = a.d, hd = a.hd, half = hd >> 1;
-    const int pos0 = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -259,6 +260,8 @@ __global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = a.M, N = a.N, K = a.K;
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 64;
+  // QKV epilogue position, read at the start so the load overlaps the main loop
+  const int pos0 = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
   const int row = lane & 31, kofs = 4 * (lane >> 5);
   const bool arow_ok = m0 + row < M;
   const float* Ap = a.A + (size_t)min(m0 + row, M - 1) * K + kofs;
@@ -339,7 +342,6 @@ __global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
     }
   } else if (EPI == EPI_QKV) {
     const int d = a.d, hd = a.hd, half = hd >> 1;
-    const int pos0 = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
     for (int e = tid; e < 32 * 32; e += blockDim.x) {
       const int rl = e >> 5, cl = 2 * (e & 31), r = m0 + rl, col = n0 + cl;
       if (r >= M || col >= N) continue;

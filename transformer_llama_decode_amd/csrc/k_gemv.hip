@@ -18,8 +18,8 @@
 //    ~2 fp64 VALU ops per weight this uses ~10% of the VALU at full bandwidth;
 //  * lane partial sums are combined with a fixed-order xor butterfly, then lane
 //    i finishes row i of the group: everything an epilogue reads (the residual
-//    row, the rotary cos/sin row) is fetched before the dot product so the
-//    wave never waits on memory between row groups;
+//    element, the rotary cos/sin of its pair) is fetched before the dot product
+//    so the wave never waits on memory between row groups;
 //  * epilogues are fused: rotary embedding + KV-cache write for Q/K/V, residual
 //    add for Wo and W2, the SwiGLU gate for W1/W3, and per-block arg-max
 //    partials for the classifier.
@@ -151,7 +151,6 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   __shared__ double red[kWavesPerBlock];
   __shared__ float best_v[kWavesPerBlock];
   __shared__ int best_i[kWavesPerBlock];
-  __shared__ float rope_cs[2 * 128];          // cos, sin row of this position (hd <= 256)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = a.K, K4 = K >> 2, N = a.N;
 
@@ -186,15 +185,9 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   const bool pre = grp < ngroups && (K4 >> 6) >= U;
   if (pre) load_batch<NR, U, NT>(wpre, rows, 0, lane);
 
-  // position of the token (rotary angle, KV-cache slot)
+  // position of the token (rotary angle, KV-cache slot); first needed by the
+  // first row group's epilogue fetch, so the load overlaps the prologue
   const int pos = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
-  if (EPI == EPI_QKV) {
-    const int half = a.hd >> 1;
-    for (int i = threadIdx.x; i < half; i += kThreads) {
-      rope_cs[i] = a.rcos[(size_t)pos * half + i];
-      rope_cs[128 + i] = a.rsin[(size_t)pos * half + i];
-    }
-  }
   stage_input(xs, a.x, a.gain, K, a.eps, red);
   const float4* xs4 = reinterpret_cast<const float4*>(xs);
 
@@ -206,6 +199,12 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
     const bool mine = lane < RW && my_r < N;
     float resid_in = 0.f;
     if (EPI == EPI_RESID && mine) resid_in = a.resid[my_r];
+    float rc_in = 1.f, rs_in = 0.f;   // rotation of the pair (my_r, my_r + 1) for q and k rows
+    if (EPI == EPI_QKV && mine && !(lane & 1) && my_r < 2 * a.d) {
+      const int ii = (my_r % a.d) % a.hd, t = pos * (a.hd >> 1) + (ii >> 1);
+      rc_in = a.rcos[t];
+      rs_in = a.rsin[t];
+    }
 
     double acc[NR];
 #pragma unroll
@@ -239,7 +238,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       float y0 = (float)pick(acc, lane), y1 = (float)pick(acc, lane + 1);
       const int d = a.d, hd = a.hd;
       const int sec = my_r / d, c = my_r - sec * d, h = c / hd, ii = c - h * hd;
-      if (sec < 2) rope_pair(y0, y1, rope_cs[ii >> 1], rope_cs[128 + (ii >> 1)], y0, y1);
+      if (sec < 2) rope_pair(y0, y1, rc_in, rs_in, y0, y1);
       if (sec == 0) {
         a.q_out[c] = y0;
         a.q_out[c + 1] = y1;

@@ -63,6 +63,7 @@ __global__ void __launch_bounds__(256) k_argmax_finalize(const float* pv, const 
   __shared__ float sv[4];
   __shared__ int si[4];
   const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int p_in = ring.ring != nullptr ? *ring.pos_dev : 0;   // issued early, used at the end
   const size_t src = ((size_t)r * row_stride + row_offset) * nparts;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -79,10 +80,9 @@ __global__ void __launch_bounds__(256) k_argmax_finalize(const float* pv, const 
     if (next) next[r] = bi;
     if (next2) next2[r] = bi;
     if (ring.ring != nullptr) {
-      // the token generated at position p (the step's input position)
-      const int p = *ring.pos_dev;
-      ring.ring[(size_t)p * gridDim.x + r] = bi;
-      if (r == 0) *ring.pos_next = p + 1;
+      // the token generated at position p_in (the step's input position)
+      ring.ring[(size_t)p_in * gridDim.x + r] = bi;
+      if (r == 0) *ring.pos_next = p_in + 1;
     }
   }
 }

@@ -42,7 +42,7 @@ enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS =
 struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
-  size_t x, xn, q, att, g, attn_part, arg_val, arg_idx, tok, next, err;
+  size_t x, xn, q, att, g, attn_part, attn_ticket, arg_val, arg_idx, tok, next, err;
   size_t pos_dev, gen;
   size_t total;
   int rows;            // R: activation rows per forward pass
@@ -90,6 +90,7 @@ struct AttnArgs {
   const float* vc;     // V cache of this layer, sequence 0
   float* out;          // [rows][d]
   double* part;        // partial (o[hd], m, l) per (row, head, chunk)
+  int* ticket;         // chunks finished per (row, head); zero between launches
   int rows, n_tok, pos, d, H, hd, seq_pad, bmax;
   const int* pos_dev;  // when set, the position is read from device memory instead of pos,
                        // and the chunk count is fixed by the cache length (graph replays)

@@ -160,9 +160,10 @@ def main():
     ap.add_argument("--workload", default="C5",
                     help="C5 (default: 7B shape, batch 1); also C1, C2, C3 (batch 256), C4, C4b32")
     ap.add_argument("--cpu-steps", type=int, default=4)
-    ap.add_argument("--eager", action="store_true",
-                    help="time one ld_decode_step call per position instead of the on-device "
-                         "generation loop (ld_generate: the step replayed as a HIP graph)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the on-device generation loop (ld_generate: the step replayed as a "
+                         "HIP graph) instead of one ld_decode_step call per position (both feed "
+                         "the greedy tokens back on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
@@ -243,7 +244,7 @@ def main():
     gen_out = torch.empty((max(steps, args.warmup), B), dtype=torch.int32, device=dev)
 
     def run_timed(k, tok):
-        if args.eager:
+        if not args.graph:
             return run(k, tok)
         gm.generate(tok, k, out=gen_out)
         return gen_out[k - 1]
@@ -341,8 +342,8 @@ def main():
             "positions": "%d..%d" % (P, P + steps - 1),
             "prompt_tokens": int(prompt.shape[1]) if w.prompt_len else 0,
             "seed": w.model_seed,
-            "loop": ("host loop of ld_decode_step" if args.eager else
-                     "ld_generate: greedy tokens fed back on the device, one HIP graph replay per position"),
+            "loop": ("ld_generate: one HIP graph replay per position" if args.graph else
+                     "ld_decode_step per position, tokens fed back on the device"),
         },
         "hbm_gbps_step": round(avg_bytes * tok_s / B / 1e9, 1),
         "hbm_frac_step": round(avg_bytes * tok_s / B / 1e9 / HBM_PEAK_GBS, 4),

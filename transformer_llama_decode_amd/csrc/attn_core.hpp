@@ -111,12 +111,15 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   // the history turns out shorter than c + 1 tiles
   const bool spec = a.pos_dev != nullptr;
   if (spec) load_tile<HD>(cur, kt, vb, c, w, lane);
+  // the query does not depend on the position either: its load goes out first
+  const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
+  const bool q_lane = threadIdx.x < HD / 4;   // HD / 4 <= 64 < kThreads
+  const float4 qv_in = q_lane ? q4[threadIdx.x] : make_float4(0.f, 0.f, 0.f, 0.f);
   const int pos = spec ? *a.pos_dev : a.pos;
   const int kvlen = pos + t + 1;
   const int ntiles = (kvlen + kTile - 1) / kTile;
   if (!spec && c < ntiles) load_tile<HD>(cur, kt, vb, c, w, lane);   // first tile in flight
-  const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
-  for (int i = threadIdx.x; i < HD / 4; i += kThreads) qs4[i] = q4[i];
+  if (q_lane) qs4[threadIdx.x] = qv_in;
   __syncthreads();
 
   double m_run = -INFINITY, l_run = 0.0;

@@ -314,6 +314,8 @@ hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
 // of U 16-byte loads per row in flight).
 hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s) { return launch<EPI_QKV, 2, 8>(a, s); }
 hipError_t launch_gemv_resid(const GemvArgs& a, hipStream_t s) {
+  // long rows (W2: K = hidden width) keep more rows in flight with one row per wave
+  if (a.K >= 8192) return launch<EPI_RESID, 1, 8>(a, s);
   return launch<EPI_RESID, 2, 8>(a, s);
 }
 hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s) {

@@ -17,6 +17,8 @@
 //    in adjacent lanes), residual add for Wo and W2, the SwiGLU gate for W1/W3
 //    (interleaved 32-row blocks put h1 and h3 of one column in the same lane),
 //    and per-row arg-max partials for the classifier.
+#include <algorithm>
+
 #include "dev_common.hpp"
 #include "ld_internal.hpp"
 
@@ -234,13 +236,20 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Split-K variant for small problems (the layer GEMMs of batched decode): a
-// workgroup owns a 32 x 64 output tile and KW waves split K between them.  Each
-// lane's global float4 loads are already the MFMA operand layout (row lane%32,
-// k offset 4*(lane/32)), so operands go straight from memory to the matrix
-// cores with no LDS staging and no barrier in the K loop; batches of SK_STEPS
-// 8-k groups are issued at once.  The KW partial tiles are summed in LDS in a
-// fixed order (in double), then a shared epilogue reads the finished tile.
-constexpr int SK_STEPS = 8;
+// workgroup of 8 waves owns a 32 x 64 output tile and the waves split K between
+// them.  K is walked in chunks of kc <= 320: the workgroup stages the chunk's 32
+// A rows and 64 W rows in LDS with row-contiguous 16-byte loads (each wave
+// instruction reads 1 KiB of consecutive memory; loading straight into the MFMA
+// operand layout would touch 32 rows, i.e. 32 cache lines, per instruction and
+// measured ~4x slower), the next chunk's loads are issued before the current
+// chunk is consumed, and wave w takes the chunk's 8-k groups w, w+8, w+16, ...
+// from LDS.  The 8 partial tiles are summed in LDS in a fixed order (in double),
+// then a shared epilogue reads the finished tile.
+constexpr int SK_WAVES = 8;
+constexpr int SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_KC = 320;   // largest K chunk staged at once
+constexpr int SK_ROWS = 96;  // 32 A rows + 64 W rows
+constexpr int SK_PER_THREAD = (SK_ROWS * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS;   // float4 slots
 
 template <bool CARRY>
 struct SkAcc {
@@ -251,23 +260,55 @@ struct SkAcc<false> {
   typedef float T;
 };
 
+// LDS bytes for chunk length kc
+size_t sk_lds_bytes(int kc, bool carry) {
+  const size_t stage = (size_t)SK_ROWS * (kc + 4) * sizeof(float);
+  const size_t red = (size_t)SK_WAVES * 2 * 16 * 64 * (carry ? 8 : 4);
+  return stage > red ? stage : red;
+}
+
 template <int EPI, bool CARRY>
-__global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
+__global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc) {
   typedef typename SkAcc<CARRY>::T PT;
   extern __shared__ char sk_smem[];
-  PT* red = reinterpret_cast<PT*>(sk_smem);   // [KW][2 tiles][16 regs][64 lanes]
-  const int KW = blockDim.x >> 6;
+  float* stg = reinterpret_cast<float*>(sk_smem);   // [96][kc + 4] while in the K loop
+  PT* red = reinterpret_cast<PT*>(sk_smem);         // [8][2 tiles][16 regs][64 lanes] afterwards
+  constexpr int KW = SK_WAVES;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = a.M, N = a.N, K = a.K;
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 64;
   // QKV epilogue position, read at the start so the load overlaps the main loop
   const int pos0 = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
+  const int ldsw = kc + 4;   // LDS row stride: a 16-byte skew from row to row
   const int row = lane & 31, kofs = 4 * (lane >> 5);
-  const bool arow_ok = m0 + row < M;
-  const float* Ap = a.A + (size_t)min(m0 + row, M - 1) * K + kofs;
-  const float* W0 = a.W + (size_t)min(n0 + row, N - 1) * K + kofs;
-  const float* W1 = a.W + (size_t)min(n0 + 32 + row, N - 1) * K + kofs;
-  const int k_begin = w * kchunk, k_end = min(K, k_begin + kchunk);
+
+  // operands the epilogue reads, fetched now so they arrive during the K loop:
+  // residual elements (thread handles outputs e = tid + i * SK_THREADS) and the
+  // rotary cos / sin of its q / k pairs (pairs e = tid + i * SK_THREADS)
+  constexpr int RES_PER = 32 * 64 / SK_THREADS, PAIR_PER = 32 * 32 / SK_THREADS;
+  float res_in[EPI == EPI_RESID ? RES_PER : 1];
+  float rc_in[EPI == EPI_QKV ? PAIR_PER : 1], rs_in[EPI == EPI_QKV ? PAIR_PER : 1];
+  if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < RES_PER; ++i) {
+      const int e = tid + i * SK_THREADS, r = m0 + (e >> 6), c = n0 + (e & 63);
+      res_in[i] = (r < M && c < N) ? a.resid[(size_t)r * N + c] : 0.f;
+    }
+  }
+  if (EPI == EPI_QKV) {
+    const int d = a.d, hd = a.hd, half = hd >> 1;
+#pragma unroll
+    for (int i = 0; i < PAIR_PER; ++i) {
+      const int e = tid + i * SK_THREADS, r = m0 + (e >> 5), col = n0 + 2 * (e & 31);
+      rc_in[i] = 1.f;
+      rs_in[i] = 0.f;
+      if (r < M && col < N && col < 2 * d) {
+        const int ii = (col % d) % hd, b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
+        rc_in[i] = a.rcos[p * half + (ii >> 1)];
+        rs_in[i] = a.rsin[p * half + (ii >> 1)];
+      }
+    }
+  }
 
   floatx16 acc0, acc1;
   double dacc[2][CARRY ? 16 : 1];
@@ -278,32 +319,61 @@ __global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
   }
 #pragma unroll
   for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[0][j] = dacc[1][j] = 0.0;
-  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = k_begin; k0 < k_end; k0 += 8 * SK_STEPS) {
-    float4 av[SK_STEPS], b0[SK_STEPS], b1[SK_STEPS];
+
+  // one chunk [kb, kb + kn) of the 96 staged rows, flat float4 index f = r * (kn/4) + c
+  float4 st[SK_PER_THREAD];
+  auto gload = [&](int kb, int kn) {
+    const int f4 = kn >> 2;
 #pragma unroll
-    for (int s = 0; s < SK_STEPS; ++s) {
-      const int kk = k0 + 8 * s;
-      if (kk < k_end) {
-        av[s] = arow_ok ? *reinterpret_cast<const float4*>(Ap + kk) : z4;
-        b0[s] = *reinterpret_cast<const float4*>(W0 + kk);
-        b1[s] = *reinterpret_cast<const float4*>(W1 + kk);
+    for (int i = 0; i < SK_PER_THREAD; ++i) {
+      const int f = tid + i * SK_THREADS;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (f < SK_ROWS * f4) {
+        const int r = f / f4, c = f - r * f4;
+        const float* src = nullptr;
+        if (r < 32) {
+          if (m0 + r < M) src = a.A + (size_t)(m0 + r) * K;
+        } else if (n0 + r - 32 < N) {
+          src = a.W + (size_t)(n0 + r - 32) * K;
+        }
+        if (src) v = *reinterpret_cast<const float4*>(src + kb + 4 * c);
+      }
+      st[i] = v;
+    }
+  };
+  auto sstore = [&](int kn) {
+    const int f4 = kn >> 2;
+#pragma unroll
+    for (int i = 0; i < SK_PER_THREAD; ++i) {
+      const int f = tid + i * SK_THREADS;
+      if (f < SK_ROWS * f4) {
+        const int r = f / f4, c = f - r * f4;
+        *reinterpret_cast<float4*>(stg + r * ldsw + 4 * c) = st[i];
       }
     }
-#pragma unroll
-    for (int s = 0; s < SK_STEPS; ++s) {
-      if (k0 + 8 * s < k_end) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].x, b0[s].x, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].y, b0[s].y, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].z, b0[s].z, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].w, b0[s].w, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].x, b1[s].x, acc1, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].y, b1[s].y, acc1, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].z, b1[s].z, acc1, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s].w, b1[s].w, acc1, 0, 0, 0);
-      }
+  };
+
+  gload(0, min(kc, K));
+  for (int kb = 0; kb < K; kb += kc) {
+    const int kn = min(kc, K - kb);
+    __syncthreads();   // every wave is done reading the previous chunk
+    sstore(kn);
+    __syncthreads();
+    if (kb + kc < K) gload(kb + kc, min(kc, K - kb - kc));   // in flight while this chunk is used
+    for (int g = w; g < (kn >> 3); g += KW) {
+      const float4 av = *reinterpret_cast<const float4*>(stg + row * ldsw + 8 * g + kofs);
+      const float4 b0 = *reinterpret_cast<const float4*>(stg + (32 + row) * ldsw + 8 * g + kofs);
+      const float4 b1 = *reinterpret_cast<const float4*>(stg + (64 + row) * ldsw + 8 * g + kofs);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0.x, acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b0.y, acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b0.z, acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b0.w, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1.y, acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b1.z, acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b1.w, acc1, 0, 0, 0);
     }
-    if (CARRY) {
+    if (CARRY) {   // at most kc / 8 / KW = 5 groups (40 k) per wave per chunk in fp32
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         dacc[0][j & (CARRY ? 15 : 0)] += (double)acc0[j];
@@ -313,6 +383,7 @@ __global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
       }
     }
   }
+  __syncthreads();   // the staging area becomes the reduction area
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     red[((w * 2 + 0) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[0][j & (CARRY ? 15 : 0)] : (PT)acc0[j];
@@ -333,25 +404,23 @@ __global__ void __launch_bounds__(512) k_gemm_sk(GemmArgs a, int kchunk) {
   };
 
   if (EPI == EPI_RESID) {
-    for (int e = tid; e < 32 * 64; e += blockDim.x) {
+#pragma unroll
+    for (int i = 0; i < RES_PER; ++i) {
+      const int e = tid + i * SK_THREADS;
       const int rl = e >> 6, cl = e & 63, r = m0 + rl, c = n0 + cl;
-      if (r < M && c < N) {
-        float* p = a.resid + (size_t)r * N + c;
-        *p = *p + tile(rl, cl);
-      }
+      if (r < M && c < N) a.resid[(size_t)r * N + c] = res_in[i] + tile(rl, cl);
     }
   } else if (EPI == EPI_QKV) {
-    const int d = a.d, hd = a.hd, half = hd >> 1;
-    for (int e = tid; e < 32 * 32; e += blockDim.x) {
+    const int d = a.d, hd = a.hd;
+#pragma unroll
+    for (int i = 0; i < PAIR_PER; ++i) {
+      const int e = tid + i * SK_THREADS;
       const int rl = e >> 5, cl = 2 * (e & 31), r = m0 + rl, col = n0 + cl;
       if (r >= M || col >= N) continue;
       float y0 = tile(rl, cl), y1 = tile(rl, cl + 1);
       const int sec = col / d, c = col - sec * d, h = c / hd, ii = c - h * hd;
       const int b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
-      if (sec < 2) {
-        const int t = p * half + (ii >> 1);
-        rope_pair(y0, y1, a.rcos[t], a.rsin[t], y0, y1);
-      }
+      if (sec < 2) rope_pair(y0, y1, rc_in[i], rs_in[i], y0, y1);
       const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * hd;
       if (sec == 0) {
         a.q_out[(size_t)r * d + c] = y0;
@@ -401,23 +470,28 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   const int nb = (a.N + 127) / 128;
   auto blocks = [&](int bm) { return ((a.M + bm - 1) / bm) * nb; };
   if (a.M <= 256 && blocks(a.M > 32 ? 64 : 32) < 256) {
-    // small problem: split K across the waves of a workgroup
-    const int tiles = ((a.N + 63) / 64) * ((a.M + 31) / 32);
-    const int kw_max = a.carry ? 4 : 8;
-    int kw = (1024 + tiles - 1) / tiles;
-    kw = kw < 1 ? 1 : (kw > kw_max ? kw_max : kw);
-    int kchunk = (a.K + kw - 1) / kw;
-    kchunk = (kchunk + 7) / 8 * 8;
-    kw = (a.K + kchunk - 1) / kchunk;
+    // small problem: split K across the 8 waves of a workgroup
+    const int kc = a.K <= SK_KC ? a.K : 256;
     dim3 grid((a.N + 63) / 64, (a.M + 31) / 32);
-    const size_t shmem = (size_t)kw * 2 * 16 * 64 * (a.carry ? 8 : 4);
+    const size_t shmem = sk_lds_bytes(kc, a.carry);
+    // the staging area may exceed the default 64 KiB dynamic LDS limit (160 KiB per CU on gfx950)
+    static bool lds_raised = false;
+    if (!lds_raised) {
+      const int most = (int)std::max(sk_lds_bytes(SK_KC, false), sk_lds_bytes(SK_KC, true));
+      hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_sk<EPI, false>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, most);
+      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_sk<EPI, true>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, most);
+      if (e1 != hipSuccess || e2 != hipSuccess) return e1 != hipSuccess ? e1 : e2;
+      lds_raised = true;
+    }
     if (nparts) *nparts = grid.x;
     if (a.carry)
-      hipExtLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(64 * kw), shmem, s, a.ev_start, a.ev_stop,
-                            0, a, kchunk);
+      hipExtLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(SK_THREADS), shmem, s, a.ev_start,
+                            a.ev_stop, 0, a, kc);
     else
-      hipExtLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(64 * kw), shmem, s, a.ev_start,
-                            a.ev_stop, 0, a, kchunk);
+      hipExtLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(SK_THREADS), shmem, s, a.ev_start,
+                            a.ev_stop, 0, a, kc);
     return hipGetLastError();
   }
   int bm;

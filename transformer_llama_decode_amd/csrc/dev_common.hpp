@@ -64,6 +64,20 @@ __device__ __forceinline__ void rope_pair(float y0, float y1, float c, float s, 
   o1 = (float)(a * ss + b * cc);
 }
 
+// Values that cross workgroups inside one launch (attention chunk partials,
+// split-K partial tiles) are written and read with relaxed device-scope atomics:
+// those are coherent across the XCDs' L2 caches without an L2-wide
+// release/acquire fence.  A writer waits for its stores to complete
+// (s_waitcnt) before taking the ticket that announces them.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Index of element (position p, dimension i) in a head's K-cache tiles
 // [Sp/64][hd/4][64][4]: within a 64-position tile, 4 consecutive dimensions of
 // one position are one float4, and lane j of a wave reading float4 column i/4

@@ -80,6 +80,8 @@ void make_layout(const ld_config* c, Layout* L) {
   L->g = take(R * f * 4);
   L->attn_part = take((size_t)kMaxAttnParts * (hd + 2) * 8);
   L->attn_ticket = take((size_t)kMaxAttnParts * 4);
+  L->sk_ws = take(kSkWorkspaceBytes);
+  L->sk_ticket = take((size_t)kSkMaxTiles * 4);
   L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
   L->arg_val = take(L->arg_parts * 4);
   L->arg_idx = take(L->arg_parts * 4);
@@ -373,6 +375,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_QKV, true);
       GemmArgs a{};
+      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = xn; a.W = m->layer(l, m->lay.o_wqkv); a.M = rows; a.N = 3 * d; a.K = d; a.carry = m->carry;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
@@ -393,6 +396,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_WO, true);
       GemmArgs a{};
+      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = att; a.W = m->layer(l, m->lay.o_wo); a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
       a.resid = x;
@@ -403,6 +407,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_W13, true);
       GemmArgs a{};
+      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = xn; a.W = m->layer(l, m->lay.o_w13); a.M = rows; a.N = 2 * f; a.K = d; a.carry = m->carry;
       a.g_out = g; a.f = f;
@@ -411,6 +416,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_W2, true);
       GemmArgs a{};
+      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = g; a.W = m->layer(l, m->lay.o_w2); a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
       a.resid = x;
@@ -454,6 +460,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
       LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->at<float>(m->lay.gain_final), B, d, n_tok, n_tok - 1,
                                      c.norm_eps, m->stream));
     GemmArgs a{};
+    a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
     a.A = xn; a.W = m->at<float>(m->lay.Wcls); a.M = cls_rows; a.N = V; a.K = d; a.carry = m->carry;
     a.logits = logits;
     a.n_tok = all_pos ? n_tok : 1;
@@ -639,6 +646,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
         hipMemsetAsync(m->arena + L.Vc, 0, L.x - L.Vc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.err, 0, 4, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.attn_ticket, 0, (size_t)kMaxAttnParts * 4, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.sk_ticket, 0, (size_t)kSkMaxTiles * 4, m->stream) != hipSuccess ||
         hipStreamSynchronize(m->stream) != hipSuccess)
       return fail(LD_E_HIP);
   }

@@ -21,19 +21,6 @@ using attn::kMaxHd;
 
 constexpr int kSplitBelow = 512;   // split heads over tiles when rows*heads is below this
 
-// Values that cross workgroups inside one launch (the chunk partials) are
-// written and read with relaxed device-scope atomics: those are coherent across
-// the XCDs' L2 caches without an L2-wide release/acquire fence.  A writer waits
-// for its stores to complete before taking the ticket that announces them.
-template <typename T>
-__device__ __forceinline__ void st_dev(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 constexpr int kMergeBatch = 16;   // chunk partials loaded at once per thread
 
 // Merge of one (row, head)'s chunk partials by the last of its workgroups:

@@ -236,15 +236,19 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Split-K variant for small problems (the layer GEMMs of batched decode): a
-// workgroup of 8 waves owns a 32 x 64 output tile and the waves split K between
-// them.  K is walked in chunks of kc <= 320: the workgroup stages the chunk's 32
+// workgroup of 8 waves owns a 32 x 64 output tile and a slice of K (grid.z
+// slices per tile when the tiles alone would leave most CUs idle), and the
+// waves split the slice between them.  The slice is walked in chunks of kc <= 320: the workgroup stages the chunk's 32
 // A rows and 64 W rows in LDS with row-contiguous 16-byte loads (each wave
 // instruction reads 1 KiB of consecutive memory; loading straight into the MFMA
 // operand layout would touch 32 rows, i.e. 32 cache lines, per instruction and
 // measured ~4x slower), the next chunk's loads are issued before the current
 // chunk is consumed, and wave w takes the chunk's 8-k groups w, w+8, w+16, ...
-// from LDS.  The 8 partial tiles are summed in LDS in a fixed order (in double),
-// then a shared epilogue reads the finished tile.
+// from LDS.  The 8 partial tiles are summed in LDS in a fixed order (in double).
+// With several K slices, each workgroup publishes its double partial tile with
+// device-coherent stores and takes a per-tile ticket; the last slice to arrive
+// sums the partials in slice order.  The finished tile is rounded once and a
+// shared epilogue reads it.
 constexpr int SK_WAVES = 8;
 constexpr int SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_KC = 320;   // largest K chunk staged at once
@@ -268,7 +272,7 @@ size_t sk_lds_bytes(int kc, bool carry) {
 }
 
 template <int EPI, bool CARRY>
-__global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc) {
+__global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int kz) {
   typedef typename SkAcc<CARRY>::T PT;
   extern __shared__ char sk_smem[];
   float* stg = reinterpret_cast<float*>(sk_smem);   // [96][kc + 4] while in the K loop
@@ -277,6 +281,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = a.M, N = a.N, K = a.K;
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 64;
+  const int ks = gridDim.z, kbeg = blockIdx.z * kz, kend = min(K, kbeg + kz);   // this K slice
   // QKV epilogue position, read at the start so the load overlaps the main loop
   const int pos0 = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
   const int ldsw = kc + 4;   // LDS row stride: a 16-byte skew from row to row
@@ -353,13 +358,13 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc) {
     }
   };
 
-  gload(0, min(kc, K));
-  for (int kb = 0; kb < K; kb += kc) {
-    const int kn = min(kc, K - kb);
+  gload(kbeg, min(kc, kend - kbeg));
+  for (int kb = kbeg; kb < kend; kb += kc) {
+    const int kn = min(kc, kend - kb);
     __syncthreads();   // every wave is done reading the previous chunk
     sstore(kn);
     __syncthreads();
-    if (kb + kc < K) gload(kb + kc, min(kc, K - kb - kc));   // in flight while this chunk is used
+    if (kb + kc < kend) gload(kb + kc, min(kc, kend - kb - kc));   // in flight while this chunk is used
     for (int g = w; g < (kn >> 3); g += KW) {
       const float4 av = *reinterpret_cast<const float4*>(stg + row * ldsw + 8 * g + kofs);
       const float4 b0 = *reinterpret_cast<const float4*>(stg + (32 + row) * ldsw + 8 * g + kofs);
@@ -390,11 +395,44 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc) {
     red[((w * 2 + 1) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[1][j & (CARRY ? 15 : 0)] : (PT)acc1[j];
   }
   __syncthreads();
-  // fixed-order sum of the KW partials, rounded once; result kept in slot w = 0
+  // fixed-order sum of the KW partials; with one K slice it is rounded once and
+  // kept in slot w = 0, else published for the last slice of the tile
+  const int tile_id = blockIdx.y * gridDim.x + blockIdx.x;
+  double* wsp = a.ws + (size_t)tile_id * ks * 2048;
   for (int e = tid; e < 2 * 16 * 64; e += blockDim.x) {
     double s = 0.0;
     for (int ww = 0; ww < KW; ++ww) s += (double)red[ww * 2 * 16 * 64 + e];
-    red[e] = (PT)(float)s;
+    if (ks == 1)
+      red[e] = (PT)(float)s;
+    else
+      st_dev(wsp + (size_t)blockIdx.z * 2048 + e, s);
+  }
+  if (ks > 1) {
+    __shared__ int is_last;
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+    __syncthreads();
+    if (tid == 0)
+      is_last = __hip_atomic_fetch_add(a.tickets + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                ks - 1;
+    __syncthreads();
+    if (!is_last) return;
+    // the last slice: sum the ks partials of every element in slice order
+    constexpr int EPT = 2048 / SK_THREADS;   // elements per thread
+    constexpr int ZB = 16;                  // partials loaded at once
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + q * SK_THREADS;
+      double acc = 0.0;
+      for (int z0 = 0; z0 < ks; z0 += ZB) {
+        double v[ZB];
+#pragma unroll
+        for (int u = 0; u < ZB; ++u) v[u] = z0 + u < ks ? ld_dev(wsp + (size_t)(z0 + u) * 2048 + e) : 0.0;
+#pragma unroll
+        for (int u = 0; u < ZB; ++u) acc += v[u];
+      }
+      red[e] = (PT)(float)acc;
+    }
+    if (tid == 0) st_dev(a.tickets + tile_id, 0);   // every slice has arrived: re-arm
   }
   __syncthreads();
   // finished value of local output (rl in 0..31, cl in 0..63)
@@ -470,9 +508,21 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   const int nb = (a.N + 127) / 128;
   auto blocks = [&](int bm) { return ((a.M + bm - 1) / bm) * nb; };
   if (a.M <= 256 && blocks(a.M > 32 ? 64 : 32) < 256) {
-    // small problem: split K across the 8 waves of a workgroup
-    const int kc = a.K <= SK_KC ? a.K : 256;
-    dim3 grid((a.N + 63) / 64, (a.M + 31) / 32);
+    // small problem: split K across the 8 waves of a workgroup, and, when there
+    // are few tiles (<= 64: measured break-even at the 15M b256 shapes), across
+    // workgroups (grid.z) until about 256 workgroups run
+    dim3 grid((a.N + 63) / 64, (a.M + 31) / 32, 1);
+    const int tiles = grid.x * grid.y;
+    int ks = 1;
+    if (a.ws != nullptr && tiles <= 64) {
+      ks = std::min(std::min((256 + tiles - 1) / tiles, kSkMaxSlices), std::max(1, a.K / 64));
+      while (ks > 1 && (size_t)tiles * ks * 2048 * sizeof(double) > kSkWorkspaceBytes) --ks;
+    }
+    int kz = (a.K + ks - 1) / ks;
+    kz = (kz + 31) / 32 * 32;
+    ks = (a.K + kz - 1) / kz;
+    grid.z = ks;
+    const int kc = kz <= SK_KC ? kz : 256;
     const size_t shmem = sk_lds_bytes(kc, a.carry);
     // the staging area may exceed the default 64 KiB dynamic LDS limit (160 KiB per CU on gfx950)
     static bool lds_raised = false;
@@ -488,10 +538,10 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     if (nparts) *nparts = grid.x;
     if (a.carry)
       hipExtLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(SK_THREADS), shmem, s, a.ev_start,
-                            a.ev_stop, 0, a, kc);
+                            a.ev_stop, 0, a, kc, kz);
     else
       hipExtLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(SK_THREADS), shmem, s, a.ev_start,
-                            a.ev_stop, 0, a, kc);
+                            a.ev_stop, 0, a, kc, kz);
     return hipGetLastError();
   }
   int bm;

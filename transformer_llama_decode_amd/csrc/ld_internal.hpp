@@ -19,7 +19,8 @@
 //                                 dimensions are contiguous (1 KiB per wave load)
 //   V cache [L][Bmax][H][Sp][hd]  position-major rows
 //   activations for up to R rows: x, xn, q, att [R][d]; g [R][f]
-//   attention partials, arg-max partials, token buffers, error flag
+//   attention partials, split-K partial tiles and tickets, arg-max partials,
+//   token buffers, error flag
 //   device position pair [pos, pos_next] and the generated-token ring
 //   [S][Bmax] of the on-device generation loop
 #pragma once
@@ -42,7 +43,7 @@ enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS =
 struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
-  size_t x, xn, q, att, g, attn_part, attn_ticket, arg_val, arg_idx, tok, next, err;
+  size_t x, xn, q, att, g, attn_part, attn_ticket, sk_ws, sk_ticket, arg_val, arg_idx, tok, next, err;
   size_t pos_dev, gen;
   size_t total;
   int rows;            // R: activation rows per forward pass
@@ -123,7 +124,15 @@ struct GemmArgs {
   float* part_val;
   int* part_idx;
   int* err;
+  // split-K across workgroups: partial tiles and per-tile tickets (zero between
+  // launches); nullptr ws keeps every tile in one workgroup
+  double* ws;
+  int* tickets;
 };
+// capacity of the split-K workspace: tiles that may be split, slices per tile, bytes
+constexpr int kSkMaxTiles = 256;
+constexpr int kSkMaxSlices = 16;
+constexpr size_t kSkWorkspaceBytes = (size_t)16 << 20;
 hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);

@@ -93,17 +93,22 @@ void or_softmax(double* s, int n) {
 }
 
 /* Causal multi-head attention of one query over n_pos cached positions
- * (Vaswani et al. 2017, eq. 1).  k_rows / v_rows are [n_pos][dim] (position
- * major); head h uses columns [h*hd, (h+1)*hd).
- *   s_j = <q_h, k_{j,h}> / sqrt(hd);  a = softmax(s);  o_h = sum_j a_j v_{j,h} */
+ * (Vaswani et al. 2017, eq. 1), with n_kv_heads key/value heads shared by
+ * groups of n_heads / n_kv_heads consecutive query heads (grouped-query
+ * attention, Ainslie et al. 2023, sec. 2.2; n_kv_heads = 1 is multi-query
+ * attention, Shazeer 2019; n_kv_heads = n_heads is plain multi-head).
+ * k_rows / v_rows are [n_pos][n_kv_heads*hd] (position major); query head h
+ * reads key/value head h / (n_heads / n_kv_heads).
+ *   s_j = <q_h, k_{j,g(h)}> / sqrt(hd);  a = softmax(s);  o_h = sum_j a_j v_{j,g(h)} */
 void or_attention(float* out, const float* q, const float* k_rows, const float* v_rows,
-                  int n_pos, int dim, int n_heads) {
-  int hd = dim / n_heads;
+                  int n_pos, int dim, int n_heads, int n_kv_heads) {
+  int hd = dim / n_heads, kvd = n_kv_heads * hd, group = n_heads / n_kv_heads;
   double* s = (double*)malloc(sizeof(double) * (size_t)n_pos);
   for (int h = 0; h < n_heads; ++h) {
     const float* qh = q + (size_t)h * hd;
+    const size_t kv_off = (size_t)(h / group) * hd;
     for (int j = 0; j < n_pos; ++j) {
-      const float* kj = k_rows + (size_t)j * dim + (size_t)h * hd;
+      const float* kj = k_rows + (size_t)j * kvd + kv_off;
       double dot = 0.0;
       for (int i = 0; i < hd; ++i) dot += (double)qh[i] * (double)kj[i];
       s[j] = dot / sqrt((double)hd);
@@ -112,7 +117,7 @@ void or_attention(float* out, const float* q, const float* k_rows, const float* 
     for (int i = 0; i < hd; ++i) {
       double acc = 0.0;
       for (int j = 0; j < n_pos; ++j)
-        acc += s[j] * (double)v_rows[(size_t)j * dim + (size_t)h * hd + i];
+        acc += s[j] * (double)v_rows[(size_t)j * kvd + kv_off + i];
       out[(size_t)h * hd + i] = (float)acc;
     }
   }
@@ -147,9 +152,10 @@ int or_argmax(const float* v, int n) {
 
 struct or_model {
   or_config c;
-  int hd;
+  int hd, kvh, kvd;                     /* head dim, key/value heads, kvh * hd */
   float* emb;                           /* [V][d]  stream 0 */
-  float **wq, **wk, **wv, **wo;         /* [L] x [d][d] */
+  float **wq, **wo;                     /* [L] x [d][d] */
+  float **wk, **wv;                     /* [L] x [kvd][d] */
   float **w1, **w3;                     /* [L] x [f][d] */
   float** w2;                           /* [L] x [d][f] */
   float *wcls;                          /* [V][d]; == emb when tied */
@@ -159,14 +165,16 @@ struct or_model {
 
 struct or_state {
   const or_model* m;
-  float *kc, *vc;                       /* [L][S][d] */
+  float *kc, *vc;                       /* [L][S][kvd] */
   float *x, *xn, *q, *k, *v, *att, *t, *h1, *h3, *g;
 };
+
+static int kv_heads(const or_config* c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
 
 static int cfg_ok(const or_config* c) {
   return c->dim > 0 && c->n_layers > 0 && c->n_heads > 0 && c->hidden_dim > 0 &&
          c->vocab_size > 0 && c->max_seq > 0 && c->dim % c->n_heads == 0 &&
-         (c->dim / c->n_heads) % 2 == 0;
+         (c->dim / c->n_heads) % 2 == 0 && c->n_kv_heads >= 0 && c->n_heads % kv_heads(c) == 0;
 }
 
 static float* draw(uint64_t seed, uint64_t stream, size_t n, int nthreads) {
@@ -188,7 +196,10 @@ or_model* or_model_create(const or_config* cfg, uint64_t seed, int nthreads) {
   if (!m) return NULL;
   m->c = *cfg;
   m->hd = cfg->dim / cfg->n_heads;
+  m->kvh = kv_heads(cfg);
+  m->kvd = m->kvh * m->hd;
   size_t d = (size_t)cfg->dim, f = (size_t)cfg->hidden_dim, V = (size_t)cfg->vocab_size;
+  size_t kvd = (size_t)m->kvd;
   int L = cfg->n_layers;
   m->wq = (float**)calloc((size_t)L, sizeof(float*));
   m->wk = (float**)calloc((size_t)L, sizeof(float*));
@@ -205,8 +216,8 @@ or_model* or_model_create(const or_config* cfg, uint64_t seed, int nthreads) {
   ok = ok && m->emb;
   for (int l = 0; ok && l < L; ++l) {
     m->wq[l] = draw(seed, synth_stream_layer(l, 0), d * d, nthreads);
-    m->wk[l] = draw(seed, synth_stream_layer(l, 1), d * d, nthreads);
-    m->wv[l] = draw(seed, synth_stream_layer(l, 2), d * d, nthreads);
+    m->wk[l] = draw(seed, synth_stream_layer(l, 1), kvd * d, nthreads);
+    m->wv[l] = draw(seed, synth_stream_layer(l, 2), kvd * d, nthreads);
     m->wo[l] = draw(seed, synth_stream_layer(l, 3), d * d, nthreads);
     m->w1[l] = draw(seed, synth_stream_layer(l, 4), f * d, nthreads);
     m->w2[l] = draw(seed, synth_stream_layer(l, 5), d * f, nthreads);
@@ -281,8 +292,8 @@ float* or_model_tensor(or_model* m, int64_t id, size_t* n) {
   int64_t l = (id - 1) / 7, kind = (id - 1) % 7;
   switch (kind) {
     case 0: if (n) *n = d * d; return m->wq[l];
-    case 1: if (n) *n = d * d; return m->wk[l];
-    case 2: if (n) *n = d * d; return m->wv[l];
+    case 1: if (n) *n = (size_t)m->kvd * d; return m->wk[l];
+    case 2: if (n) *n = (size_t)m->kvd * d; return m->wv[l];
     case 3: if (n) *n = d * d; return m->wo[l];
     case 4: if (n) *n = f * d; return m->w1[l];
     case 5: if (n) *n = d * f; return m->w2[l];
@@ -295,7 +306,7 @@ or_state* or_state_create(const or_model* m) {
   if (!s) return NULL;
   s->m = m;
   size_t d = (size_t)m->c.dim, f = (size_t)m->c.hidden_dim;
-  size_t kv = (size_t)m->c.n_layers * (size_t)m->c.max_seq * d;
+  size_t kv = (size_t)m->c.n_layers * (size_t)m->c.max_seq * (size_t)m->kvd;
   s->kc = (float*)calloc(kv, sizeof(float));
   s->vc = (float*)calloc(kv, sizeof(float));
   s->x = (float*)malloc(sizeof(float) * d);
@@ -346,21 +357,21 @@ static int head(const or_model* m, const float* x, float* xn, float* logits) {
 int or_forward(const or_model* m, or_state* s, int token, int pos, float* logits) {
   const or_config* c = &m->c;
   if (token < 0 || token >= c->vocab_size || pos < 0 || pos >= c->max_seq) return -2;
-  int d = c->dim, hd = m->hd, half = hd / 2;
+  int d = c->dim, hd = m->hd, half = hd / 2, kvd = m->kvd;
   memcpy(s->x, m->emb + (size_t)token * d, sizeof(float) * (size_t)d);
   for (int l = 0; l < c->n_layers; ++l) {
-    float* kl = s->kc + (size_t)l * c->max_seq * d;
-    float* vl = s->vc + (size_t)l * c->max_seq * d;
+    float* kl = s->kc + (size_t)l * c->max_seq * kvd;
+    float* vl = s->vc + (size_t)l * c->max_seq * kvd;
     /* attention half: x <- x + Wo attn(rope(Wq n(x)), cache) */
     or_rmsnorm(s->xn, s->x, m->att_gain[l], d, c->norm_eps);
     or_matvec(s->q, m->wq[l], s->xn, d, d);
-    or_matvec(s->k, m->wk[l], s->xn, d, d);
-    or_matvec(s->v, m->wv[l], s->xn, d, d);
+    or_matvec(s->k, m->wk[l], s->xn, kvd, d);
+    or_matvec(s->v, m->wv[l], s->xn, kvd, d);
     or_rope(s->q, d, hd, m->rope_cos + (size_t)pos * half, m->rope_sin + (size_t)pos * half);
-    or_rope(s->k, d, hd, m->rope_cos + (size_t)pos * half, m->rope_sin + (size_t)pos * half);
-    memcpy(kl + (size_t)pos * d, s->k, sizeof(float) * (size_t)d);
-    memcpy(vl + (size_t)pos * d, s->v, sizeof(float) * (size_t)d);
-    or_attention(s->att, s->q, kl, vl, pos + 1, d, c->n_heads);
+    or_rope(s->k, kvd, hd, m->rope_cos + (size_t)pos * half, m->rope_sin + (size_t)pos * half);
+    memcpy(kl + (size_t)pos * kvd, s->k, sizeof(float) * (size_t)kvd);
+    memcpy(vl + (size_t)pos * kvd, s->v, sizeof(float) * (size_t)kvd);
+    or_attention(s->att, s->q, kl, vl, pos + 1, d, c->n_heads, m->kvh);
     or_matvec(s->t, m->wo[l], s->att, d, d);
     or_residual_add(s->x, s->t, d);
     ffn_block(m, l, s->x, s->xn, s->h1, s->h3, s->g, s->t);
@@ -373,12 +384,12 @@ int or_forward_recompute(const or_model* m, const int* tokens, int n, float* log
   if (n <= 0 || n > c->max_seq) return -2;
   for (int i = 0; i < n; ++i)
     if (tokens[i] < 0 || tokens[i] >= c->vocab_size) return -2;
-  size_t d = (size_t)c->dim, f = (size_t)c->hidden_dim;
+  size_t d = (size_t)c->dim, f = (size_t)c->hidden_dim, kvd = (size_t)m->kvd;
   int hd = m->hd, half = hd / 2;
   /* every position's residual stream, and this layer's K and V for all positions */
   float* X = (float*)malloc(sizeof(float) * n * d);
-  float* K = (float*)malloc(sizeof(float) * n * d);
-  float* Vv = (float*)malloc(sizeof(float) * n * d);
+  float* K = (float*)malloc(sizeof(float) * n * kvd);
+  float* Vv = (float*)malloc(sizeof(float) * n * kvd);
   float* xn = (float*)malloc(sizeof(float) * d);
   float* q = (float*)malloc(sizeof(float) * d);
   float* att = (float*)malloc(sizeof(float) * d);
@@ -394,9 +405,9 @@ int or_forward_recompute(const or_model* m, const int* tokens, int n, float* log
     /* keys and values of every position from the layer input */
     for (int i = 0; i < n; ++i) {
       or_rmsnorm(xn, X + (size_t)i * d, m->att_gain[l], (int)d, c->norm_eps);
-      or_matvec(K + (size_t)i * d, m->wk[l], xn, (int)d, (int)d);
-      or_matvec(Vv + (size_t)i * d, m->wv[l], xn, (int)d, (int)d);
-      or_rope(K + (size_t)i * d, (int)d, hd, m->rope_cos + (size_t)i * half,
+      or_matvec(K + (size_t)i * kvd, m->wk[l], xn, (int)kvd, (int)d);
+      or_matvec(Vv + (size_t)i * kvd, m->wv[l], xn, (int)kvd, (int)d);
+      or_rope(K + (size_t)i * kvd, (int)kvd, hd, m->rope_cos + (size_t)i * half,
               m->rope_sin + (size_t)i * half);
     }
     /* then each position attends to positions 0..i */
@@ -405,7 +416,7 @@ int or_forward_recompute(const or_model* m, const int* tokens, int n, float* log
       or_rmsnorm(xn, x, m->att_gain[l], (int)d, c->norm_eps);
       or_matvec(q, m->wq[l], xn, (int)d, (int)d);
       or_rope(q, (int)d, hd, m->rope_cos + (size_t)i * half, m->rope_sin + (size_t)i * half);
-      or_attention(att, q, K, Vv, i + 1, (int)d, c->n_heads);
+      or_attention(att, q, K, Vv, i + 1, (int)d, c->n_heads, m->kvh);
       or_matvec(t, m->wo[l], att, (int)d, (int)d);
       or_residual_add(x, t, (int)d);
       ffn_block(m, l, x, xn, h1, h3, g, t);

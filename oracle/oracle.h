@@ -23,8 +23,9 @@
 extern "C" {
 #endif
 
+/* n_kv_heads: key/value heads (grouped-query attention); 0 means n_heads. */
 typedef struct {
-  int32_t dim, n_layers, n_heads, hidden_dim, vocab_size, max_seq, tied;
+  int32_t dim, n_layers, n_heads, hidden_dim, vocab_size, max_seq, tied, n_kv_heads;
   double rope_theta, norm_eps;
 } or_config;
 
@@ -38,7 +39,7 @@ void or_rope_table(float* cos_t, float* sin_t, int max_seq, int head_dim, double
 void or_rope(float* v, int dim, int head_dim, const float* cos_row, const float* sin_row);
 void or_softmax(double* s, int n);
 void or_attention(float* out, const float* q, const float* k_rows, const float* v_rows,
-                  int n_pos, int dim, int n_heads);
+                  int n_pos, int dim, int n_heads, int n_kv_heads);
 void or_swiglu(float* g, const float* h1, const float* h3, int n);
 void or_residual_add(float* x, const float* t, int n);
 int or_argmax(const float* v, int n);

@@ -21,7 +21,8 @@ I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 class OrConfig(C.Structure):
     _fields_ = [("dim", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
                 ("hidden_dim", C.c_int32), ("vocab_size", C.c_int32), ("max_seq", C.c_int32),
-                ("tied", C.c_int32), ("rope_theta", C.c_double), ("norm_eps", C.c_double)]
+                ("tied", C.c_int32), ("n_kv_heads", C.c_int32), ("rope_theta", C.c_double),
+                ("norm_eps", C.c_double)]
 
 
 def lib(path=None):
@@ -47,7 +48,7 @@ def _bind(L):
     L.or_rope_table.argtypes = [F32P, F32P, C.c_int, C.c_int, C.c_double]
     L.or_rope.argtypes = [F32P, C.c_int, C.c_int, F32P, F32P]
     L.or_softmax.argtypes = [F64P, C.c_int]
-    L.or_attention.argtypes = [F32P, F32P, F32P, F32P, C.c_int, C.c_int, C.c_int]
+    L.or_attention.argtypes = [F32P, F32P, F32P, F32P, C.c_int, C.c_int, C.c_int, C.c_int]
     L.or_swiglu.argtypes = [F32P, F32P, F32P, C.c_int]
     L.or_residual_add.argtypes = [F32P, F32P, C.c_int]
     L.or_argmax.argtypes = [F32P, C.c_int]
@@ -116,12 +117,14 @@ def softmax(s, L=None):
     return s
 
 
-def attention(q, k_rows, v_rows, n_heads, L=None):
+def attention(q, k_rows, v_rows, n_heads, n_kv_heads=None, L=None):
+    """k_rows, v_rows: [n_pos][n_kv_heads * head_dim] (n_kv_heads defaults to n_heads)"""
     L = L or lib()
     q = _f32(q)
     k_rows = _f32(k_rows)
     out = np.empty_like(q)
-    L.or_attention(out, q, k_rows, _f32(v_rows), k_rows.shape[0], q.size, n_heads)
+    L.or_attention(out, q, k_rows, _f32(v_rows), k_rows.shape[0], q.size, n_heads,
+                   n_heads if n_kv_heads is None else n_kv_heads)
     return out
 
 
@@ -168,14 +171,15 @@ class OracleModel:
     """One model instance: weights drawn from `seed` (std 0.02, gains 1.0).
 
     cfg is any object with attributes dim, n_layers, n_heads, hidden_dim,
-    vocab_size, max_seq, tied, rope_theta, norm_eps.
+    vocab_size, max_seq, tied, rope_theta, norm_eps (and optionally n_kv_heads).
     """
 
     def __init__(self, cfg, seed, nthreads=8, L=None):
         self.L = L or lib()
         self.cfg = cfg
         c = OrConfig(cfg.dim, cfg.n_layers, cfg.n_heads, cfg.hidden_dim, cfg.vocab_size,
-                     cfg.max_seq, int(cfg.tied), float(cfg.rope_theta), float(cfg.norm_eps))
+                     cfg.max_seq, int(cfg.tied), int(getattr(cfg, "n_kv_heads", 0) or 0),
+                     float(cfg.rope_theta), float(cfg.norm_eps))
         self._h = self.L.or_model_create(C.byref(c), seed, nthreads)
         if not self._h:
             raise ValueError("oracle rejected config %r" % (cfg,))

@@ -31,19 +31,23 @@ MUTANTS = {
     "rope_half_split_pairs": ("double a = vh[2 * i], b = vh[2 * i + 1];",
                               "double a = vh[i], b = vh[i + half];"),
     "rope_frequency_exponent": ("-(2.0 * (double)i) / (double)head_dim", "-(double)i / (double)head_dim"),
-    "rope_not_applied_to_k": ("    or_rope(s->k, d, hd,", "    if (0) or_rope(s->k, d, hd,"),
+    "rope_not_applied_to_k": ("    or_rope(s->k, kvd, hd,", "    if (0) or_rope(s->k, kvd, hd,"),
     "attention_scale_1_over_hd": ("dot / sqrt((double)hd)", "dot / (double)hd"),
     "attention_excludes_current_position": ("or_attention(s->att, s->q, kl, vl, pos + 1,",
                                             "or_attention(s->att, s->q, kl, vl, pos > 0 ? pos : 1,"),
-    "attention_v_head_offset": ("v_rows[(size_t)j * dim + (size_t)h * hd + i]", "v_rows[(size_t)j * dim + i]"),
+    "attention_v_head_offset": ("v_rows[(size_t)j * kvd + kv_off + i]", "v_rows[(size_t)j * kvd + i]"),
+    "gqa_kv_head_modulo": ("const size_t kv_off = (size_t)(h / group) * hd;",
+                           "const size_t kv_off = (size_t)(h % n_kv_heads) * hd;"),
+    "gqa_key_row_stride_dim": ("const float* kj = k_rows + (size_t)j * kvd + kv_off;",
+                               "const float* kj = k_rows + (size_t)j * dim + kv_off;"),
     "softmax_not_normalised": ("for (int j = 0; j < n; ++j) s[j] /= sum;", ""),
     "swiglu_gate_on_w3": ("double z = h1[i];\n    g[i] = (float)((z / (1.0 + exp(-z))) * (double)h3[i]);",
                           "double z = h3[i];\n    g[i] = (float)((z / (1.0 + exp(-z))) * (double)h1[i]);"),
     "silu_sign": ("(z / (1.0 + exp(-z)))", "(z / (1.0 + exp(z)))"),
     "residual_dropped": ("x[i] = x[i] + t[i];", "x[i] = t[i];"),
-    "cache_written_one_back": ("memcpy(kl + (size_t)pos * d, s->k",
-                               "memcpy(kl + (size_t)(pos > 0 ? pos - 1 : 0) * d, s->k"),
-    "value_cache_gets_keys": ("memcpy(vl + (size_t)pos * d, s->v", "memcpy(vl + (size_t)pos * d, s->k"),
+    "cache_written_one_back": ("memcpy(kl + (size_t)pos * kvd, s->k",
+                               "memcpy(kl + (size_t)(pos > 0 ? pos - 1 : 0) * kvd, s->k"),
+    "value_cache_gets_keys": ("memcpy(vl + (size_t)pos * kvd, s->v", "memcpy(vl + (size_t)pos * kvd, s->k"),
     "query_uses_wk": ("or_matvec(s->q, m->wq[l], s->xn, d, d);", "or_matvec(s->q, m->wk[l], s->xn, d, d);"),
     "argmax_highest_index_on_ties": ("if (v[i] > v[best]) best = i;", "if (v[i] >= v[best]) best = i;"),
     "classifier_ignores_untied": ("or_matvec(logits, m->wcls, xn,", "or_matvec(logits, m->emb, xn,"),

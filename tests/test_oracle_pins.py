@@ -352,3 +352,73 @@ def test_weights_come_from_the_generator():
         w = m.tensor(sid)
         assert np.array_equal(w, O.synth_normal(5, sid, 0, w.size))
     assert np.all(m.tensor(-1) == 1.0) and np.all(m.tensor(-1 - 2 * L) == 1.0)
+
+
+# ------------------------------------------------ grouped-query attention ----
+# n_kv_heads key/value heads, each shared by n_heads / n_kv_heads consecutive
+# query heads (Ainslie et al. 2023, sec. 2.2); one key/value head is multi-query
+# attention (the pages' "multi-query support" TODO).
+GQA = ModelConfig(dim=64, n_layers=2, n_heads=4, hidden_dim=96, vocab_size=301, max_seq=24,
+                  tied=False, n_kv_heads=2)
+MQA = ModelConfig(dim=64, n_layers=2, n_heads=4, hidden_dim=96, vocab_size=301, max_seq=24,
+                  tied=True, n_kv_heads=1)
+
+
+def test_gqa_attention_equals_mha_with_repeated_kv_heads():
+    r = _rng(31)
+    H, hd, n = 6, 8, 5
+    for Hkv in (1, 2, 3, 6):
+        g = H // Hkv
+        q = r.standard_normal(H * hd).astype(np.float32)
+        k = r.standard_normal((n, Hkv * hd)).astype(np.float32)
+        v = r.standard_normal((n, Hkv * hd)).astype(np.float32)
+        # MHA head h gets key/value head h // g (np.repeat keeps each head's hd columns together)
+        k_rep = np.repeat(k.reshape(n, Hkv, hd), g, axis=1).reshape(n, H * hd)
+        v_rep = np.repeat(v.reshape(n, Hkv, hd), g, axis=1).reshape(n, H * hd)
+        assert np.array_equal(O.attention(q, k, v, H, Hkv), O.attention(q, k_rep, v_rep, H)), Hkv
+
+
+@pytest.mark.parametrize("cfg", [GQA, MQA])
+def test_gqa_model_equals_mha_model_with_repeated_kv_rows(cfg):
+    """A GQA model and an MHA model whose Wk / Wv repeat each key/value head's
+    rows for its query-head group give bit-identical logits."""
+    seed = 33
+    gm = O.OracleModel(cfg, seed)
+    mha = ModelConfig(**{**cfg.__dict__, "n_kv_heads": 0})
+    mm = O.OracleModel(mha, seed)
+    H, Hkv, hd, d = cfg.n_heads, cfg.kv_heads, cfg.head_dim, cfg.dim
+    g = H // Hkv
+    for l in range(cfg.n_layers):
+        for kind in (1, 2):                       # Wk, Wv of layer l
+            sid = 1 + 7 * l + kind
+            src = gm.tensor(sid).reshape(Hkv, hd, d)
+            mm.tensor(sid)[:] = np.repeat(src, g, axis=0).reshape(-1)
+    toks = O.synth_prompt(seed, 0, cfg.max_seq, 0, cfg.vocab_size)
+    s1, s2 = gm.new_state(), mm.new_state()
+    for p in range(cfg.max_seq):
+        r1, l1 = gm.forward(s1, int(toks[p]), p)
+        r2, l2 = mm.forward(s2, int(toks[p]), p)
+        assert r1 == r2 and np.array_equal(l1, l2), p
+
+
+@pytest.mark.parametrize("cfg,seed", [(GQA, 34), (MQA, 35)])
+def test_gqa_incremental_cache_equals_full_recomputation(cfg, seed):
+    m = O.OracleModel(cfg, seed)
+    toks = O.synth_prompt(seed, 0, cfg.max_seq, 0, cfg.vocab_size)
+    st = m.new_state()
+    for p in range(cfg.max_seq):
+        r, logits = m.forward(st, int(toks[p]), p)
+        r2, logits2 = m.recompute(toks[: p + 1])
+        assert r == r2
+        assert np.array_equal(logits, logits2), p
+
+
+def test_gqa_weight_shapes_and_bad_head_counts():
+    m = O.OracleModel(GQA, 36)
+    kvd = GQA.kv_dim
+    assert m.tensor(2).size == kvd * GQA.dim and m.tensor(3).size == kvd * GQA.dim   # Wk, Wv
+    assert m.tensor(1).size == GQA.dim * GQA.dim                                   # Wq
+    assert np.array_equal(m.tensor(2), O.synth_normal(36, 2, 0, kvd * GQA.dim))
+    with pytest.raises(ValueError):
+        O.OracleModel(ModelConfig(dim=64, n_layers=1, n_heads=4, hidden_dim=32, vocab_size=10,
+                                  max_seq=4, n_kv_heads=3), 1)

@@ -24,20 +24,29 @@ class ModelConfig:
     rope_theta: float = 10000.0
     norm_eps: float = 1e-5
     max_batch: int = 1
+    n_kv_heads: int = 0          # key/value heads (grouped-query attention); 0 = n_heads
 
     @property
     def head_dim(self):
         return self.dim // self.n_heads
 
+    @property
+    def kv_heads(self):
+        return self.n_kv_heads or self.n_heads
+
+    @property
+    def kv_dim(self):
+        return self.kv_heads * self.head_dim
+
     def n_params(self):
         d, f, V, L = self.dim, self.hidden_dim, self.vocab_size, self.n_layers
-        per_layer = 4 * d * d + 3 * d * f + 2 * d
+        per_layer = 2 * d * d + 2 * self.kv_dim * d + 3 * d * f + 2 * d
         return V * d + L * per_layer + d + (0 if self.tied else V * d)
 
     def weight_bytes(self):
         """fp32 bytes of every matrix the decode step streams once per token."""
         d, f, V, L = self.dim, self.hidden_dim, self.vocab_size, self.n_layers
-        return 4 * (L * (4 * d * d + 3 * d * f) + V * d)
+        return 4 * (L * (2 * d * d + 2 * self.kv_dim * d + 3 * d * f) + V * d)
 
 
 @dataclass(frozen=True)

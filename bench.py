@@ -38,10 +38,10 @@ def step_bytes(cfg, pos, batch=1):
     """Algorithmic HBM bytes of one decode step at position pos: every matrix
     once, plus per sequence the embedding row, norm gains, the K/V history read
     (positions 0..pos), the new K/V written and the logits written."""
-    d, f, V, L = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers
-    weights = 4 * (L * (4 * d * d + 3 * d * f) + V * d)
+    d, f, V, L, kvd = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers, cfg.kv_dim
+    weights = 4 * (L * (2 * d * d + 2 * kvd * d + 3 * d * f) + V * d)
     gains = 4 * (2 * L + 1) * d
-    per_seq = 4 * (d + 2 * L * (pos + 1) * d + 2 * L * d + V)
+    per_seq = 4 * (d + 2 * L * (pos + 1) * kvd + 2 * L * kvd + V)
     return weights + gains + batch * per_seq
 
 
@@ -148,8 +148,8 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out
 
 def gemm_flops_per_step(cfg, batch):
     """Algorithmic flops of every projection of one decode step for `batch` rows."""
-    d, f, V, L = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers
-    return 2 * batch * (L * (4 * d * d + 3 * d * f) + V * d)
+    d, f, V, L, kvd = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers, cfg.kv_dim
+    return 2 * batch * (L * (2 * d * d + 2 * kvd * d + 3 * d * f) + V * d)
 
 
 def main():

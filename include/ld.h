@@ -55,6 +55,12 @@ typedef struct {
   int32_t max_seq;         /* positions held by the KV cache */
   int32_t max_batch;       /* sequences decoded in lockstep, >= 1 */
   int32_t tied_classifier; /* 1: classifier = token embedding; 0: separate matrix */
+  int32_t n_kv_heads;      /* key/value heads, dividing n_heads; 0 = n_heads.  Fewer than
+                              n_heads is grouped-query attention: query head h reads
+                              key/value head h / (n_heads / n_kv_heads) (Ainslie et al.
+                              2023, sec. 2.2); 1 is multi-query attention, the pages'
+                              TODO (openai.wiki "llama2.c | Baby LLaMA", "Unsorted TODO").
+                              Wk and Wv are then [n_kv_heads * head_dim][dim]. */
   double rope_theta;       /* rotary base, 10000 for Llama-2 */
   double norm_eps;         /* RMSNorm epsilon, added inside the square root */
 } ld_config;

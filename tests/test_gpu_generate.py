@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from transformer_llama_decode_amd.configs import TINY, TINY_UNTIED, SMALL, ModelConfig
+from transformer_llama_decode_amd.configs import TINY, TINY_UNTIED, SMALL, TINY_GQA, SMALL_MQA, ModelConfig
 from tests.parity import assert_logits, assert_token
 
 pytestmark = pytest.mark.gpu
@@ -57,6 +57,9 @@ CASES = [
     (SMALL, 9, 3),
     (ModelConfig(dim=96, n_layers=2, n_heads=6, hidden_dim=160, vocab_size=777, max_seq=70,
                  max_batch=3), 10, 2),
+    (TINY_GQA, 17, 1),
+    (TINY_GQA, 17, 5),
+    (SMALL_MQA, 18, 3),
 ]
 
 

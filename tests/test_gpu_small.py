@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from transformer_llama_decode_amd.configs import TINY, TINY_UNTIED, SMALL, ModelConfig
+from transformer_llama_decode_amd.configs import (TINY, TINY_UNTIED, SMALL, TINY_GQA, SMALL_MQA,
+                                                   GQA_HD64, ModelConfig)
 from tests.parity import assert_logits, assert_token
 
 pytestmark = pytest.mark.gpu
@@ -57,6 +58,10 @@ CASES = [
     (SMALL, 9),
     (ModelConfig(dim=96, n_layers=2, n_heads=6, hidden_dim=160, vocab_size=777, max_seq=70,
                  max_batch=3), 10),
+    # grouped-query / multi-query attention (key/value heads shared by query-head groups)
+    (TINY_GQA, 17),
+    (SMALL_MQA, 18),
+    (GQA_HD64, 19),
 ]
 
 
@@ -71,7 +76,8 @@ def test_weights_on_device_are_the_generator_values(dev, cfg, seed):
             n = cfg.vocab_size * cfg.dim
         else:
             kind = (sid - 1) % 7
-            n = cfg.dim * (cfg.hidden_dim if kind in (4, 5, 6) else cfg.dim)
+            n = cfg.dim * (cfg.hidden_dim if kind in (4, 5, 6) else
+                           cfg.kv_dim if kind in (1, 2) else cfg.dim)
         got = gm.read_weights(sid, 0, n)
         want = O.synth_normal(seed, sid, 0, n)
         assert np.array_equal(got, want), sid
@@ -158,7 +164,7 @@ def test_batched_lockstep_matches_each_sequence_alone(dev, cfg, seed):
     gm.close()
 
 
-@pytest.mark.parametrize("cfg,seed", [(TINY, 11), (SMALL, 12)])
+@pytest.mark.parametrize("cfg,seed", [(TINY, 11), (SMALL, 12), (SMALL_MQA, 13)])
 def test_many_row_prefill_every_logit(dev, cfg, seed):
     # more than 256 rows per forward pass: the LDS-tiled MFMA GEMM path
     # (smaller row counts take the split-K path exercised above)

@@ -65,7 +65,7 @@ def _cfg(m, **kw):
 @pytest.mark.parametrize("bad", [dict(dim=100), dict(n_heads=5), dict(hidden_dim=100), dict(vocab_size=0),
                                  dict(max_seq=0), dict(max_batch=0), dict(rope_theta=0.0),
                                  dict(dim=64, n_heads=1, hidden_dim=64, vocab_size=10, max_seq=4) | {"n_layers": 0},
-                                 dict(dim=512, n_heads=1)])
+                                 dict(dim=512, n_heads=1), dict(n_kv_heads=3), dict(n_kv_heads=-1)])
 def test_arena_bytes_rejects_unsupported_configs(L, bad):
     n = C.c_size_t(0)
     assert L.ld_arena_bytes(C.byref(_cfg(TINY, **bad)), C.byref(n)) == _lib.LD_E_INVAL
@@ -97,3 +97,18 @@ def test_prompt_generator_is_the_shared_one(L):
     from transformer_llama_decode_amd.model import synth_prompt
     for seed, seq in [(1, 0), (2, 255), (4, 0)]:
         assert np.array_equal(synth_prompt(seed, seq, 512), O.synth_prompt(seed, seq, 512))
+
+
+def test_grouped_query_arena_saves_the_key_value_rows_and_cache(L):
+    from dataclasses import replace
+    mha = ModelConfig(dim=256, n_layers=2, n_heads=8, hidden_dim=320, vocab_size=301, max_seq=128,
+                      max_batch=3)
+    sizes = {}
+    for kvh in (0, 2, 1):
+        n = C.c_size_t(0)
+        assert L.ld_arena_bytes(C.byref(_cfg(replace(mha, n_kv_heads=kvh))), C.byref(n)) == 0
+        sizes[kvh] = n.value
+    hd, d, Lr, B, S = 32, 256, 2, 3, 128
+    for kvh in (2, 1):
+        saved = 4 * Lr * (2 * (d - kvh * hd) * d + 2 * B * S * (d - kvh * hd))
+        assert abs((sizes[0] - sizes[kvh]) - saved) <= 8 * 256, kvh

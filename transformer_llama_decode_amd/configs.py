@@ -92,6 +92,11 @@ WORKLOADS = {
     "C5": Workload("C5", M7B, 4, 1, 512, 4, 1024,
                    description="7B shape (4096/32L/32H, 11008 hidden), b1, 512-token prompt, "
                                "512 decode steps"),
+    # grouped-query variant of the 7B shape: 8 key/value heads shared by groups of 4
+    # query heads (a measurement of the grouped-query row; not one of the five configs)
+    "C5g8": Workload("C5g8", replace(M7B, n_kv_heads=8), 4, 1, 512, 4, 1024,
+                     description="7B shape with 8 key/value heads (grouped-query), b1, "
+                                 "512-token prompt, 512 decode steps"),
 }
 
 # Small shapes for element-by-element parity: several tiles and ragged tails.
@@ -100,3 +105,10 @@ TINY = ModelConfig(dim=64, n_layers=2, n_heads=4, hidden_dim=96, vocab_size=1003
 TINY_UNTIED = replace(TINY, tied=False, n_heads=2, vocab_size=517)
 SMALL = ModelConfig(dim=128, n_layers=3, n_heads=2, hidden_dim=352, vocab_size=4099,
                     max_seq=160, max_batch=7)
+# grouped-query shapes: 2 key/value heads for 4 query heads (head dim 16), one
+# key/value head for 4 query heads (multi-query, head dim 32), and head dim 64
+TINY_GQA = replace(TINY, n_kv_heads=2)
+SMALL_MQA = ModelConfig(dim=128, n_layers=3, n_heads=4, hidden_dim=352, vocab_size=4099,
+                        max_seq=160, max_batch=7, n_kv_heads=1)
+GQA_HD64 = ModelConfig(dim=256, n_layers=2, n_heads=4, hidden_dim=320, vocab_size=2011,
+                       max_seq=200, max_batch=4, n_kv_heads=2)

@@ -101,7 +101,8 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   __shared__ double es[kTile];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = r / a.n_tok, t = r - b * a.n_tok;
-  const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * HD;
+  // key/value head of query head h (grouped-query attention: H / kvh query heads share one)
+  const size_t head_off = ((size_t)b * a.kvh + h / (a.H / a.kvh)) * (size_t)a.seq_pad * HD;
   const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);   // [Sp/64][HD/4][64] float4
   const float* vb = a.vc + head_off;                                      // [Sp][HD]
   const double sqrt_hd = sqrt((double)HD);

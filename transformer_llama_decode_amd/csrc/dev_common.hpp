@@ -78,6 +78,22 @@ __device__ __forceinline__ T ld_dev(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Section of index col of the fused [q; k; v] projection output (q: d rows, k
+// and v: kvd = key/value heads * head_dim rows each): 0 query, 1 key, 2 value;
+// *c receives the index inside the section.
+__device__ __forceinline__ int qkv_section(int col, int d, int kvd, int* c) {
+  if (col < d) {
+    *c = col;
+    return 0;
+  }
+  if (col < d + kvd) {
+    *c = col - d;
+    return 1;
+  }
+  *c = col - d - kvd;
+  return 2;
+}
+
 // Index of element (position p, dimension i) in a head's K-cache tiles
 // [Sp/64][hd/4][64][4]: within a 64-position tile, 4 consecutive dimensions of
 // one position are one float4, and lane j of a wave reading float4 column i/4

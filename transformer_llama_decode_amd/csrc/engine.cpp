@@ -30,11 +30,15 @@ constexpr int kProfPairs = 1 << 15;   // event pairs per profiled kernel class
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// key/value heads (grouped-query attention); 0 in the config means n_heads
+int kv_heads(const ld_config* c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
+
 int validate(const ld_config* c) {
   if (c == nullptr) return LD_E_INVAL;
   if (c->dim <= 0 || c->dim % 32 != 0 || c->dim > 16384) return LD_E_INVAL;
   if (c->n_layers <= 0 || c->n_layers > 1024) return LD_E_INVAL;
   if (c->n_heads <= 0 || c->dim % c->n_heads != 0) return LD_E_INVAL;
+  if (c->n_kv_heads < 0 || (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0)) return LD_E_INVAL;
   const int hd = c->dim / c->n_heads;
   if (hd % 16 != 0 || hd > 256) return LD_E_INVAL;
   if (c->hidden_dim <= 0 || c->hidden_dim % 32 != 0 || c->hidden_dim > 65536) return LD_E_INVAL;
@@ -48,6 +52,7 @@ int validate(const ld_config* c) {
 void make_layout(const ld_config* c, Layout* L) {
   const size_t d = c->dim, f = c->hidden_dim, V = c->vocab_size, NL = c->n_layers,
                H = c->n_heads, hd = d / H, S = c->max_seq, B = c->max_batch;
+  const size_t kvd = (size_t)kv_heads(c) * hd;   // rows of Wk and of Wv
   const size_t Sp = round_up(S, 64);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -57,7 +62,7 @@ void make_layout(const ld_config* c, Layout* L) {
   };
   L->E = take(V * d * 4);
   L->o_wqkv = 0;
-  L->o_wo = L->o_wqkv + round_up(3 * d * d * 4, kAlign);
+  L->o_wo = L->o_wqkv + round_up((d + 2 * kvd) * d * 4, kAlign);
   L->o_w13 = L->o_wo + round_up(d * d * 4, kAlign);
   L->o_w2 = L->o_w13 + round_up(2 * f * d * 4, kAlign);
   L->o_gatt = L->o_w2 + round_up(d * f * 4, kAlign);
@@ -68,8 +73,8 @@ void make_layout(const ld_config* c, Layout* L) {
   L->gain_final = take(d * 4);
   L->rope_cos = take(S * (hd / 2) * 4);
   L->rope_sin = take(S * (hd / 2) * 4);
-  L->Kc = take(NL * B * H * Sp * hd * 4);
-  L->Vc = take(NL * B * H * Sp * hd * 4);
+  L->Kc = take(NL * B * kvd * Sp * 4);
+  L->Vc = take(NL * B * kvd * Sp * 4);
   const size_t R = std::max(B, std::min((size_t)kMaxRowsCap, B * S));
   L->rows = (int)R;
   L->seq_pad = (int)Sp;
@@ -104,7 +109,7 @@ struct Prof {
 struct ld_model {
   ld_config c;
   Layout lay;
-  int hd, device;
+  int hd, kvh, kvd, device;   // head dim, key/value heads, kvh * hd
   hipStream_t stream;
   char* arena;
   int pos;
@@ -126,10 +131,10 @@ struct ld_model {
   T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
   float* layer(int l, size_t o) const { return at<float>(lay.layer0 + (size_t)l * lay.layer_stride + o); }
   float* kc(int l) const {
-    return at<float>(lay.Kc) + (size_t)l * c.max_batch * c.n_heads * lay.seq_pad * hd;
+    return at<float>(lay.Kc) + (size_t)l * c.max_batch * kvh * lay.seq_pad * hd;
   }
   float* vc(int l) const {
-    return at<float>(lay.Vc) + (size_t)l * c.max_batch * c.n_heads * lay.seq_pad * hd;
+    return at<float>(lay.Vc) + (size_t)l * c.max_batch * kvh * lay.seq_pad * hd;
   }
 };
 
@@ -315,10 +320,11 @@ int layers_gemv(ld_model* m, int pos) {
       GemvArgs a{};
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = x; a.gain = m->layer(l, m->lay.o_gatt); a.eps = c.norm_eps;
-      a.W = m->layer(l, m->lay.o_wqkv); a.N = 3 * d; a.K = d; a.stream = m->stream_weights;
+      a.W = m->layer(l, m->lay.o_wqkv); a.N = d + 2 * m->kvd; a.K = d; a.stream = m->stream_weights;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
       a.pos = pos; a.d = d; a.hd = m->hd; a.seq_pad = m->lay.seq_pad; a.pos_dev = pos_dev;
+      a.kvh = m->kvh;
       LD_TRY_HIP(launch_gemv_qkv(a, m->stream));
     }
     {
@@ -327,7 +333,7 @@ int layers_gemv(ld_model* m, int pos) {
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
       a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
-      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev; a.kvh = m->kvh;
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
@@ -377,7 +383,8 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = xn; a.W = m->layer(l, m->lay.o_wqkv); a.M = rows; a.N = 3 * d; a.K = d; a.carry = m->carry;
+      a.A = xn; a.W = m->layer(l, m->lay.o_wqkv); a.M = rows; a.N = d + 2 * m->kvd; a.K = d;
+      a.carry = m->carry; a.kvh = m->kvh;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
       a.pos = pos; a.n_tok = n_tok; a.d = d; a.hd = m->hd; a.H = c.n_heads;
@@ -390,7 +397,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
       a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
-      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev;
+      a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev; a.kvh = m->kvh;
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
@@ -563,13 +570,15 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
   m->c = *cfg;
   m->lay = L;
   m->hd = cfg->dim / cfg->n_heads;
+  m->kvh = kv_heads(cfg);
+  m->kvd = m->kvh * m->hd;
   m->stream = reinterpret_cast<hipStream_t>(hip_stream);
   m->arena = reinterpret_cast<char*>(dev_arena);
   m->pos = 0;
   // fp32 MFMA sums are carried into fp64 for wide models (K >= 2048)
   m->carry = cfg->dim >= 2048;
   {
-    const size_t wbytes = 4 * ((size_t)cfg->n_layers * (4 * (size_t)cfg->dim * cfg->dim +
+    const size_t wbytes = 4 * ((size_t)cfg->n_layers * ((2 * (size_t)cfg->dim + 2 * (size_t)m->kvd) * cfg->dim +
                                                           3 * (size_t)cfg->dim * cfg->hidden_dim) +
                                (size_t)cfg->vocab_size * cfg->dim * (cfg->tied_classifier ? 1 : 2));
     m->stream_weights = wbytes > ((size_t)256 << 20);
@@ -614,9 +623,10 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
     up.plain(m->at<float>(L.E), synth_stream_embedding(), V * d);
     for (int l = 0; l < cfg->n_layers && up.ok; ++l) {
       float* wqkv = m->layer(l, L.o_wqkv);
+      const size_t kvd = (size_t)m->kvd;
       up.plain(wqkv, synth_stream_layer(l, 0), d * d);
-      up.plain(wqkv + d * d, synth_stream_layer(l, 1), d * d);
-      up.plain(wqkv + 2 * d * d, synth_stream_layer(l, 2), d * d);
+      up.plain(wqkv + d * d, synth_stream_layer(l, 1), kvd * d);
+      up.plain(wqkv + d * d + kvd * d, synth_stream_layer(l, 2), kvd * d);
       up.plain(m->layer(l, L.o_wo), synth_stream_layer(l, 3), d * d);
       up.w13(m->layer(l, L.o_w13), synth_stream_layer(l, 4), synth_stream_layer(l, 6), f, d);
       up.plain(m->layer(l, L.o_w2), synth_stream_layer(l, 5), d * f);
@@ -778,8 +788,11 @@ int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, 
     kind = (int)((stream_id - 1) % 7);
     switch (kind) {
       case 0: base = m->layer(layer, m->lay.o_wqkv); total = d * d; break;
-      case 1: base = m->layer(layer, m->lay.o_wqkv) + d * d; total = d * d; break;
-      case 2: base = m->layer(layer, m->lay.o_wqkv) + 2 * d * d; total = d * d; break;
+      case 1: base = m->layer(layer, m->lay.o_wqkv) + d * d; total = (uint64_t)m->kvd * d; break;
+      case 2:
+        base = m->layer(layer, m->lay.o_wqkv) + d * d + (uint64_t)m->kvd * d;
+        total = (uint64_t)m->kvd * d;
+        break;
       case 3: base = m->layer(layer, m->lay.o_wo); total = d * d; break;
       case 5: base = m->layer(layer, m->lay.o_w2); total = d * f; break;
       default: base = m->layer(layer, m->lay.o_w13); total = f * d; break;   // W1 (4), W3 (6)

@@ -128,6 +128,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.kvh <= 0 || a.H % a.kvh != 0) return hipErrorInvalidValue;
   const int units = a.rows * a.H;
   int nchunk = 1;
   if (units < kSplitBelow) {

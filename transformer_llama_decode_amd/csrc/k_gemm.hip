@@ -174,14 +174,15 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           if (row >= M || col >= N) continue;
           const bool odd = col & 1;
           float y0 = odd ? partner : v, y1 = odd ? v : partner;
-          const int sec = col / d, c = col - sec * d, h = c / hd, ii = c - h * hd;
+          int c;
+          const int sec = qkv_section(col, d, a.kvh * hd, &c), h = c / hd, ii = c - h * hd;
           const int b = row / a.n_tok, p = pos0 + (row - b * a.n_tok);
           if (sec < 2) {
             const int t = p * half + (ii >> 1);
             rope_pair(y0, y1, a.rcos[t], a.rsin[t], y0, y1);
           }
           const float out = odd ? y1 : y0;
-          const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * hd;
+          const size_t head_off = ((size_t)b * a.kvh + h) * (size_t)a.seq_pad * hd;   // k, v
           if (sec == 0)
             a.q_out[(size_t)row * d + c] = out;
           else if (sec == 1)
@@ -307,7 +308,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
       const int e = tid + i * SK_THREADS, r = m0 + (e >> 5), col = n0 + 2 * (e & 31);
       rc_in[i] = 1.f;
       rs_in[i] = 0.f;
-      if (r < M && col < N && col < 2 * d) {
+      if (r < M && col < N && col < d + a.kvh * hd) {
         const int ii = (col % d) % hd, b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
         rc_in[i] = a.rcos[p * half + (ii >> 1)];
         rs_in[i] = a.rsin[p * half + (ii >> 1)];
@@ -456,10 +457,11 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
       const int rl = e >> 5, cl = 2 * (e & 31), r = m0 + rl, col = n0 + cl;
       if (r >= M || col >= N) continue;
       float y0 = tile(rl, cl), y1 = tile(rl, cl + 1);
-      const int sec = col / d, c = col - sec * d, h = c / hd, ii = c - h * hd;
+      int c;
+      const int sec = qkv_section(col, d, a.kvh * hd, &c), h = c / hd, ii = c - h * hd;
       const int b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
       if (sec < 2) rope_pair(y0, y1, rc_in[i], rs_in[i], y0, y1);
-      const size_t head_off = ((size_t)b * a.H + h) * (size_t)a.seq_pad * hd;
+      const size_t head_off = ((size_t)b * a.kvh + h) * (size_t)a.seq_pad * hd;   // k, v
       if (sec == 0) {
         a.q_out[(size_t)r * d + c] = y0;
         a.q_out[(size_t)r * d + c + 1] = y1;
@@ -573,7 +575,10 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
 
 }  // namespace
 
-hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s) { return launch<EPI_QKV>(a, s, nullptr); }
+hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s) {
+  if (a.kvh <= 0 || a.N != a.d + 2 * a.kvh * a.hd) return hipErrorInvalidValue;
+  return launch<EPI_QKV>(a, s, nullptr);
+}
 hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s) {
   return launch<EPI_RESID>(a, s, nullptr);
 }

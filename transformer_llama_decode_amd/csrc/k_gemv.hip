@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
     float resid_in = 0.f;
     if (EPI == EPI_RESID && mine) resid_in = a.resid[my_r];
     float rc_in = 1.f, rs_in = 0.f;   // rotation of the pair (my_r, my_r + 1) for q and k rows
-    if (EPI == EPI_QKV && mine && !(lane & 1) && my_r < 2 * a.d) {
+    if (EPI == EPI_QKV && mine && !(lane & 1) && my_r < a.d + a.kvh * a.hd) {
       const int ii = (my_r % a.d) % a.hd, t = pos * (a.hd >> 1) + (ii >> 1);
       rc_in = a.rcos[t];
       rs_in = a.rsin[t];
@@ -237,7 +237,8 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       if (lane & 1) continue;
       float y0 = (float)pick(acc, lane), y1 = (float)pick(acc, lane + 1);
       const int d = a.d, hd = a.hd;
-      const int sec = my_r / d, c = my_r - sec * d, h = c / hd, ii = c - h * hd;
+      int c;
+      const int sec = qkv_section(my_r, d, a.kvh * hd, &c), h = c / hd, ii = c - h * hd;
       if (sec < 2) rope_pair(y0, y1, rc_in, rs_in, y0, y1);
       if (sec == 0) {
         a.q_out[c] = y0;
@@ -312,7 +313,10 @@ hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
 
 // Shapes measured best on MI355X at the 7B sizes (rows per wave RW, batches
 // of U 16-byte loads per row in flight).
-hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s) { return launch<EPI_QKV, 2, 8>(a, s); }
+hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s) {
+  if (a.kvh <= 0 || a.N != a.d + 2 * a.kvh * a.hd) return hipErrorInvalidValue;
+  return launch<EPI_QKV, 2, 8>(a, s);
+}
 hipError_t launch_gemv_resid(const GemvArgs& a, hipStream_t s) {
   // long rows (W2: K = hidden width) keep more rows in flight with one row per wave
   if (a.K >= 8192) return launch<EPI_RESID, 1, 8>(a, s);

@@ -67,6 +67,7 @@ struct GemvArgs {
   const float* rcos;
   const float* rsin;
   int pos, d, hd, seq_pad;
+  int kvh;             // key/value heads: the k and v sections have kvh * hd rows each
   const int* pos_dev;  // when set, the position is read from device memory instead of pos
   // residual epilogue
   float* resid;
@@ -93,6 +94,7 @@ struct AttnArgs {
   double* part;        // partial (o[hd], m, l) per (row, head, chunk)
   int* ticket;         // chunks finished per (row, head); zero between launches
   int rows, n_tok, pos, d, H, hd, seq_pad, bmax;
+  int kvh;             // key/value heads; query head h reads key/value head h / (H / kvh)
   const int* pos_dev;  // when set, the position is read from device memory instead of pos,
                        // and the chunk count is fixed by the cache length (graph replays)
 };
@@ -111,6 +113,7 @@ struct GemmArgs {
   const float* rcos;
   const float* rsin;
   int pos, n_tok, d, hd, H, seq_pad, bmax;
+  int kvh;             // key/value heads: the k and v sections have kvh * hd columns each
   const int* pos_dev;  // when set, the position is read from device memory instead of pos
   // residual
   float* resid;

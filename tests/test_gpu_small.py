@@ -264,3 +264,42 @@ def test_out_of_range_device_token_is_reported(dev):
     assert gm.status() == 0          # cleared after reporting
     gm.close()
 
+
+
+LONG = [
+    (ModelConfig(dim=128, n_layers=2, n_heads=4, hidden_dim=160, vocab_size=1001, max_seq=330,
+                 max_batch=2), 41),
+    (ModelConfig(dim=256, n_layers=2, n_heads=4, hidden_dim=192, vocab_size=1001, max_seq=330,
+                 max_batch=2, n_kv_heads=2), 42),
+]
+
+
+@pytest.mark.parametrize("cfg,seed", LONG)
+def test_long_prompt_prefill_every_logit(dev, cfg, seed):
+    """prompts past 4 tiles: consecutive rows share each K/V tile in one workgroup"""
+    _say("long prompt", cfg)
+    gm, om = _models(cfg, seed)
+    B, P = 2, 301                           # ragged: 301 rows = 37 groups of 8 + 5
+    prompts = np.stack([O.synth_prompt(seed, 20 + b, P, 0, cfg.vocab_size) for b in range(B)])
+    allp = torch.empty((B, P, cfg.vocab_size), dtype=torch.float32, device=dev)
+    nxt = gm.prefill(prompts, logits=allp, all_pos=True)
+    allp = allp.cpu().numpy()
+    nn = nxt.cpu().numpy()
+    for b in range(B):
+        _, ref = _oracle_stream(om, prompts[b], P)
+        for p in range(P):
+            assert_logits(allp[b, p], ref[p], "seq %d pos %d" % (b, p))
+        assert_token(nn[b], ref[P - 1], "seq %d next" % b)
+    # then decode on top of the prompt's cache
+    lg = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device=dev)
+    feed, refs = [], []
+    for b in range(B):
+        f, r = _oracle_stream(om, prompts[b], P + 8)
+        feed.append(f)
+        refs.append(r)
+    for p in range(P, P + 8):
+        gm.decode_step(np.array([feed[b][p] for b in range(B)], np.int32), logits=lg)
+        g = lg.cpu().numpy()
+        for b in range(B):
+            assert_logits(g[b], refs[b][p], "seq %d decode pos %d" % (b, p))
+    gm.close()

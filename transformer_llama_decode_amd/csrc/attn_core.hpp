@@ -187,3 +187,117 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
 
 }  // namespace attn
 }  // namespace ld
+
+namespace ld {
+namespace attn {
+
+// R consecutive query rows t0 .. t0+nrows-1 of one sequence and one head (a
+// prompt being processed): every K/V tile is loaded once and used by all the
+// rows, instead of once per row.  The arithmetic of each row -- score chains,
+// their order, the online softmax, the weighted values -- is exactly that of
+// attn_unit with one chunk, so each row's output is bit-identical to the
+// one-row path.  Row r's output goes to out_rows[r * d + h * HD + i].
+template <int HD, int R>
+__device__ __forceinline__ void attn_rows(const AttnArgs a, int h, int b, int t0, int nrows,
+                                          float* out_rows) {
+  constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
+  __shared__ float4 qs4[R][kMaxHd / 4];
+  __shared__ double sp[4][kTile];
+  __shared__ double es[kTile];
+  __shared__ double owr[4][kMaxHd];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t head_off = ((size_t)b * a.kvh + h / (a.H / a.kvh)) * (size_t)a.seq_pad * HD;
+  const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);
+  const float* vb = a.vc + head_off;
+  const double sqrt_hd = sqrt((double)HD);
+  const int pos = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
+  const int kvlen_max = pos + t0 + nrows;   // history of the last row
+  const int ntiles = (kvlen_max + kTile - 1) / kTile;
+
+  TileRegs<HD> cur;
+  load_tile<HD>(cur, kt, vb, 0, w, lane);
+  for (int i = threadIdx.x; i < R * (HD / 4); i += kThreads) {
+    const int rr = i / (HD / 4), c4 = i - rr * (HD / 4);
+    qs4[rr][c4] = rr < nrows ? reinterpret_cast<const float4*>(
+                                   a.q + ((size_t)b * a.n_tok + t0 + rr) * a.d + (size_t)h * HD)[c4]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  double m_run[R], l_run[R], o[R][DPL];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    m_run[rr] = -INFINITY;
+    l_run[rr] = 0.0;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[rr][k] = 0.0;
+  }
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int j0 = tile * kTile;
+    mask_tile<HD>(cur, tile, kvlen_max, w);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int kvlen = pos + t0 + rr + 1;
+      if (rr >= nrows || j0 >= kvlen) continue;   // uniform: this tile is past row rr's history
+      double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) {
+        const float4 qv = qs4[rr][w * KQ + i];
+        s4[0] = fma((double)qv.x, (double)cur.k[i].x, s4[0]);
+        s4[1] = fma((double)qv.y, (double)cur.k[i].y, s4[1]);
+        s4[2] = fma((double)qv.z, (double)cur.k[i].z, s4[2]);
+        s4[3] = fma((double)qv.w, (double)cur.k[i].w, s4[3]);
+      }
+      sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      __syncthreads();
+      const bool valid = j0 + lane < kvlen;
+      const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
+      const double m_new = fmax(m_run[rr], wave_max(valid ? sc : -INFINITY));
+      const double scale = exp(m_run[rr] - m_new);
+      const double e = valid ? exp(sc - m_new) : 0.0;
+      if (w == 0) es[lane] = e;
+      l_run[rr] = l_run[rr] * scale + wave_sum(e);
+      __syncthreads();
+      double oo[DPL][2];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        oo[k][0] = o[rr][k] * scale;
+        oo[k][1] = 0.0;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const double ej = es[16 * w + jj];   // 0 past this row's history
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) oo[k][jj & 1] = fma(ej, (double)cur.v[jj][k], oo[k][jj & 1]);
+      }
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[rr][k] = oo[k][0] + oo[k][1];
+      m_run[rr] = m_new;
+    }
+    if (tile + 1 < ntiles) load_tile<HD>(cur, kt, vb, tile + 1, w, lane);
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr >= nrows) break;
+    __syncthreads();   // owr is reused row after row
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int i = lane * DPL + k;
+      if (i < HD) owr[w][i] = o[rr][k];
+    }
+    __syncthreads();
+    if (w == 0) {
+      float* out = out_rows + (size_t)rr * a.d + (size_t)h * HD;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int i = lane * DPL + k;
+        if (i < HD) out[i] = (float)((((owr[0][i] + owr[1][i]) + owr[2][i]) + owr[3][i]) / l_run[rr]);
+      }
+    }
+  }
+}
+
+}  // namespace attn
+}  // namespace ld

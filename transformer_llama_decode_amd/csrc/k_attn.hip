@@ -125,11 +125,43 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
   if (threadIdx.x == 0) st_dev(a.ticket + unit, 0);   // every chunk has arrived: re-arm
 }
 
+// Prompt rows: workgroup (h, z) takes rows t0 .. t0 + kRowsPerBlock - 1 of
+// sequence z / groups (z % groups = t0 / kRowsPerBlock), every K/V tile loaded
+// once for all of them.
+constexpr int kRowsPerBlock = 8;
+
+template <int HD>
+__global__ void __launch_bounds__(kThreads) k_attn_rows(AttnArgs a, int groups) {
+  const int h = blockIdx.y, z = blockIdx.z;
+  const int b = z / groups, t0 = (z - b * groups) * kRowsPerBlock;
+  const int nrows = min(kRowsPerBlock, a.n_tok - t0);
+  attn::attn_rows<HD, kRowsPerBlock>(a, h, b, t0, nrows, a.out + ((size_t)b * a.n_tok + t0) * a.d);
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.kvh <= 0 || a.H % a.kvh != 0) return hipErrorInvalidValue;
   const int units = a.rows * a.H;
+  if (a.n_tok > 1 && units >= kSplitBelow && a.pos + a.n_tok > 4 * kTile) {
+    // a long prompt with enough (row, head) pairs to fill the GPU without
+    // splitting heads: groups of consecutive rows share every K/V tile (with
+    // histories of a few tiles the shared loads do not pay for the rows each
+    // workgroup then walks in sequence: measured slower at 16 and 128 tokens)
+    const int groups = (a.n_tok + kRowsPerBlock - 1) / kRowsPerBlock;
+    dim3 grid(1, a.H, (a.rows / a.n_tok) * groups);
+    switch (a.hd) {
+#define LD_ATTN_ROWS_CASE(HD) \
+      case HD: hipLaunchKernelGGL((k_attn_rows<HD>), grid, dim3(kThreads), 0, s, a, groups); break;
+      LD_ATTN_ROWS_CASE(16) LD_ATTN_ROWS_CASE(32) LD_ATTN_ROWS_CASE(48) LD_ATTN_ROWS_CASE(64)
+      LD_ATTN_ROWS_CASE(80) LD_ATTN_ROWS_CASE(96) LD_ATTN_ROWS_CASE(112) LD_ATTN_ROWS_CASE(128)
+      LD_ATTN_ROWS_CASE(144) LD_ATTN_ROWS_CASE(160) LD_ATTN_ROWS_CASE(176) LD_ATTN_ROWS_CASE(192)
+      LD_ATTN_ROWS_CASE(208) LD_ATTN_ROWS_CASE(224) LD_ATTN_ROWS_CASE(240) LD_ATTN_ROWS_CASE(256)
+#undef LD_ATTN_ROWS_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   int nchunk = 1;
   if (units < kSplitBelow) {
     if (a.pos_dev != nullptr) {

@@ -267,16 +267,25 @@ def test_out_of_range_device_token_is_reported(dev):
 
 
 LONG = [
+    # head dim 32 and 64 (grouped-query): the matrix-core prompt attention
     (ModelConfig(dim=128, n_layers=2, n_heads=4, hidden_dim=160, vocab_size=1001, max_seq=330,
                  max_batch=2), 41),
     (ModelConfig(dim=256, n_layers=2, n_heads=4, hidden_dim=192, vocab_size=1001, max_seq=330,
                  max_batch=2, n_kv_heads=2), 42),
+    # head dim 96 (three 32-dimension output tiles) and 128 (multi-query)
+    (ModelConfig(dim=192, n_layers=2, n_heads=2, hidden_dim=160, vocab_size=1001, max_seq=330,
+                 max_batch=2), 43),
+    (ModelConfig(dim=256, n_layers=2, n_heads=2, hidden_dim=192, vocab_size=1001, max_seq=330,
+                 max_batch=2, n_kv_heads=1), 44),
+    # head dim 48: not a multiple of 32, rows share K/V tiles on the vector units
+    (ModelConfig(dim=192, n_layers=2, n_heads=4, hidden_dim=160, vocab_size=1001, max_seq=330,
+                 max_batch=2), 45),
 ]
 
 
 @pytest.mark.parametrize("cfg,seed", LONG)
 def test_long_prompt_prefill_every_logit(dev, cfg, seed):
-    """prompts past 4 tiles: consecutive rows share each K/V tile in one workgroup"""
+    """prompts of 301 rows (ragged against 32-row and 8-row groups, 64-key tiles)"""
     _say("long prompt", cfg)
     gm, om = _models(cfg, seed)
     B, P = 2, 301                           # ragged: 301 rows = 37 groups of 8 + 5
@@ -302,4 +311,26 @@ def test_long_prompt_prefill_every_logit(dev, cfg, seed):
         g = lg.cpu().numpy()
         for b in range(B):
             assert_logits(g[b], refs[b][p], "seq %d decode pos %d" % (b, p))
+    gm.close()
+
+
+@pytest.mark.parametrize("cfg,seed", [LONG[1], LONG[3]])
+def test_prompt_in_two_pieces_every_logit(dev, cfg, seed):
+    """a prompt fed as 100 + 201 tokens: the second piece attends to the first
+    piece's cache entries at positions below its own rows"""
+    _say("prompt in two pieces", cfg)
+    gm, om = _models(cfg, seed)
+    B, P1, P2 = 2, 100, 201
+    prompts = np.stack([O.synth_prompt(seed, 30 + b, P1 + P2, 0, cfg.vocab_size) for b in range(B)])
+    gm.prefill(prompts[:, :P1])
+    allp = torch.empty((B, P2, cfg.vocab_size), dtype=torch.float32, device=dev)
+    nxt = gm.prefill(prompts[:, P1:], logits=allp, all_pos=True)
+    assert gm.pos == P1 + P2
+    allp = allp.cpu().numpy()
+    nn = nxt.cpu().numpy()
+    for b in range(B):
+        _, ref = _oracle_stream(om, prompts[b], P1 + P2)
+        for i in range(P2):
+            assert_logits(allp[b, i], ref[P1 + i], "seq %d pos %d" % (b, P1 + i))
+        assert_token(nn[b], ref[P1 + P2 - 1], "seq %d next" % b)
     gm.close()

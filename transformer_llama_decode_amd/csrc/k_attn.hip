@@ -142,6 +142,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_rows(AttnArgs a, int groups) 
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.kvh <= 0 || a.H % a.kvh != 0) return hipErrorInvalidValue;
+  if (attention_prefill_supported(a)) return launch_attention_prefill(a, s);
   const int units = a.rows * a.H;
   if (a.n_tok > 1 && units >= kSplitBelow && a.pos + a.n_tok > 4 * kTile) {
     // a long prompt with enough (row, head) pairs to fill the GPU without

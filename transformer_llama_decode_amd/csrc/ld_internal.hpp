@@ -99,6 +99,9 @@ struct AttnArgs {
                        // and the chunk count is fixed by the cache length (graph replays)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// prompts of 32 or more rows on the matrix cores (head_dim a multiple of 32, at most 256)
+bool attention_prefill_supported(const AttnArgs& a);
+hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s);
 
 struct GemmArgs {
   const float* A;      // [M][K]

@@ -16,6 +16,14 @@
  *   KV cache          keys/values of earlier positions are kept and reused, as
  *                     the pages' TODO on running past max_seq_len implies
  *                     (openai.wiki "llama2.c | Baby LLaMA", "Unsorted TODO")
+ *   past max_seq      that TODO leaves the semantics open; read here as a
+ *                     sliding window: position p attends to the max_seq most
+ *                     recent positions (Beltagy et al. 2020, Longformer, sec.
+ *                     3.1; Jiang et al. 2023, Mistral 7B, sec. 2), rotary
+ *                     angles of the absolute position
+ *   bf16 weights      the pages' engine is fp32 only (openai.wiki, intro);
+ *                     optionally every matrix is held as bfloat16, the draw
+ *                     rounded to nearest, ties to even (or_bf16_round)
  *   greedy decoding   the next token is the arg-max logit (lowest index on ties)
  *
  * Nothing here is blocked, fused or reordered: each function is the definition
@@ -90,6 +98,26 @@ void or_softmax(double* s, int n) {
     sum += s[j];
   }
   for (int j = 0; j < n; ++j) s[j] /= sum;
+}
+
+/* bfloat16 keeps the sign, the 8 exponent bits and the top 7 fraction bits of
+ * an IEEE binary32 (Kalamkar et al. 2019, "A Study of BFLOAT16 for Deep
+ * Learning Training", sec. 2).  Rounding to nearest, ties to even, on the bit
+ * pattern: add 0x7FFF plus the lowest kept bit, then clear the 16 dropped bits
+ * (a carry out of the fraction moves into the exponent, as rounding requires;
+ * past the largest bfloat16 it gives infinity).  NaN stays NaN. */
+float or_bf16_round(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) {
+    u |= 0x00400000u;   /* quiet NaN, payload bits that survive */
+  } else {
+    u += 0x7FFFu + ((u >> 16) & 1u);
+  }
+  u &= 0xFFFF0000u;
+  float y;
+  memcpy(&y, &u, sizeof y);
+  return y;
 }
 
 /* Causal multi-head attention of one query over n_pos cached positions
@@ -171,15 +199,24 @@ struct or_state {
 
 static int kv_heads(const or_config* c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
 
+/* positions the model may run through */
+static int max_pos(const or_config* c) { return c->max_pos > 0 ? c->max_pos : c->max_seq; }
+
 static int cfg_ok(const or_config* c) {
   return c->dim > 0 && c->n_layers > 0 && c->n_heads > 0 && c->hidden_dim > 0 &&
          c->vocab_size > 0 && c->max_seq > 0 && c->dim % c->n_heads == 0 &&
-         (c->dim / c->n_heads) % 2 == 0 && c->n_kv_heads >= 0 && c->n_heads % kv_heads(c) == 0;
+         (c->dim / c->n_heads) % 2 == 0 && c->n_kv_heads >= 0 && c->n_heads % kv_heads(c) == 0 &&
+         (c->weight_bf16 == 0 || c->weight_bf16 == 1) && c->max_pos >= 0 &&
+         max_pos(c) >= c->max_seq;
 }
 
-static float* draw(uint64_t seed, uint64_t stream, size_t n, int nthreads) {
+/* a weight matrix: the generator's draw, rounded to bfloat16 when configured */
+static float* draw(const or_config* c, uint64_t seed, uint64_t stream, size_t n, int nthreads) {
   float* p = (float*)malloc(sizeof(float) * n);
-  if (p) synth_normal_mt(p, seed, stream, 0, n, 0.02, nthreads);
+  if (!p) return NULL;
+  synth_normal_mt(p, seed, stream, 0, n, 0.02, nthreads);
+  if (c->weight_bf16)
+    for (size_t i = 0; i < n; ++i) p[i] = or_bf16_round(p[i]);
   return p;
 }
 
@@ -212,16 +249,16 @@ or_model* or_model_create(const or_config* cfg, uint64_t seed, int nthreads) {
   m->ffn_gain = (float**)calloc((size_t)L, sizeof(float*));
   int ok = m->wq && m->wk && m->wv && m->wo && m->w1 && m->w2 && m->w3 && m->att_gain &&
            m->ffn_gain;
-  if (ok) m->emb = draw(seed, synth_stream_embedding(), V * d, nthreads);
+  if (ok) m->emb = draw(cfg, seed, synth_stream_embedding(), V * d, nthreads);
   ok = ok && m->emb;
   for (int l = 0; ok && l < L; ++l) {
-    m->wq[l] = draw(seed, synth_stream_layer(l, 0), d * d, nthreads);
-    m->wk[l] = draw(seed, synth_stream_layer(l, 1), kvd * d, nthreads);
-    m->wv[l] = draw(seed, synth_stream_layer(l, 2), kvd * d, nthreads);
-    m->wo[l] = draw(seed, synth_stream_layer(l, 3), d * d, nthreads);
-    m->w1[l] = draw(seed, synth_stream_layer(l, 4), f * d, nthreads);
-    m->w2[l] = draw(seed, synth_stream_layer(l, 5), d * f, nthreads);
-    m->w3[l] = draw(seed, synth_stream_layer(l, 6), f * d, nthreads);
+    m->wq[l] = draw(cfg, seed, synth_stream_layer(l, 0), d * d, nthreads);
+    m->wk[l] = draw(cfg, seed, synth_stream_layer(l, 1), kvd * d, nthreads);
+    m->wv[l] = draw(cfg, seed, synth_stream_layer(l, 2), kvd * d, nthreads);
+    m->wo[l] = draw(cfg, seed, synth_stream_layer(l, 3), d * d, nthreads);
+    m->w1[l] = draw(cfg, seed, synth_stream_layer(l, 4), f * d, nthreads);
+    m->w2[l] = draw(cfg, seed, synth_stream_layer(l, 5), d * f, nthreads);
+    m->w3[l] = draw(cfg, seed, synth_stream_layer(l, 6), f * d, nthreads);
     m->att_gain[l] = ones(d);
     m->ffn_gain[l] = ones(d);
     ok = m->wq[l] && m->wk[l] && m->wv[l] && m->wo[l] && m->w1[l] && m->w2[l] && m->w3[l] &&
@@ -229,12 +266,12 @@ or_model* or_model_create(const or_config* cfg, uint64_t seed, int nthreads) {
   }
   if (ok) {
     m->final_gain = ones(d);
-    m->wcls = cfg->tied ? m->emb : draw(seed, synth_stream_classifier(L), V * d, nthreads);
+    m->wcls = cfg->tied ? m->emb : draw(cfg, seed, synth_stream_classifier(L), V * d, nthreads);
     size_t half = (size_t)m->hd / 2;
-    m->rope_cos = (float*)malloc(sizeof(float) * (size_t)cfg->max_seq * half);
-    m->rope_sin = (float*)malloc(sizeof(float) * (size_t)cfg->max_seq * half);
+    m->rope_cos = (float*)malloc(sizeof(float) * (size_t)max_pos(cfg) * half);
+    m->rope_sin = (float*)malloc(sizeof(float) * (size_t)max_pos(cfg) * half);
     ok = m->final_gain && m->wcls && m->rope_cos && m->rope_sin;
-    if (ok) or_rope_table(m->rope_cos, m->rope_sin, cfg->max_seq, m->hd, cfg->rope_theta);
+    if (ok) or_rope_table(m->rope_cos, m->rope_sin, max_pos(cfg), m->hd, cfg->rope_theta);
   }
   if (!ok) {
     or_model_free(m);
@@ -306,7 +343,8 @@ or_state* or_state_create(const or_model* m) {
   if (!s) return NULL;
   s->m = m;
   size_t d = (size_t)m->c.dim, f = (size_t)m->c.hidden_dim;
-  size_t kv = (size_t)m->c.n_layers * (size_t)m->c.max_seq * (size_t)m->kvd;
+  /* every position's keys and values (the window only limits what is read) */
+  size_t kv = (size_t)m->c.n_layers * (size_t)max_pos(&m->c) * (size_t)m->kvd;
   s->kc = (float*)calloc(kv, sizeof(float));
   s->vc = (float*)calloc(kv, sizeof(float));
   s->x = (float*)malloc(sizeof(float) * d);
@@ -356,12 +394,14 @@ static int head(const or_model* m, const float* x, float* xn, float* logits) {
 
 int or_forward(const or_model* m, or_state* s, int token, int pos, float* logits) {
   const or_config* c = &m->c;
-  if (token < 0 || token >= c->vocab_size || pos < 0 || pos >= c->max_seq) return -2;
+  if (token < 0 || token >= c->vocab_size || pos < 0 || pos >= max_pos(c)) return -2;
   int d = c->dim, hd = m->hd, half = hd / 2, kvd = m->kvd;
+  /* the window: positions lo .. pos */
+  int lo = pos - c->max_seq + 1 > 0 ? pos - c->max_seq + 1 : 0;
   memcpy(s->x, m->emb + (size_t)token * d, sizeof(float) * (size_t)d);
   for (int l = 0; l < c->n_layers; ++l) {
-    float* kl = s->kc + (size_t)l * c->max_seq * kvd;
-    float* vl = s->vc + (size_t)l * c->max_seq * kvd;
+    float* kl = s->kc + (size_t)l * max_pos(c) * kvd;
+    float* vl = s->vc + (size_t)l * max_pos(c) * kvd;
     /* attention half: x <- x + Wo attn(rope(Wq n(x)), cache) */
     or_rmsnorm(s->xn, s->x, m->att_gain[l], d, c->norm_eps);
     or_matvec(s->q, m->wq[l], s->xn, d, d);
@@ -371,7 +411,8 @@ int or_forward(const or_model* m, or_state* s, int token, int pos, float* logits
     or_rope(s->k, kvd, hd, m->rope_cos + (size_t)pos * half, m->rope_sin + (size_t)pos * half);
     memcpy(kl + (size_t)pos * kvd, s->k, sizeof(float) * (size_t)kvd);
     memcpy(vl + (size_t)pos * kvd, s->v, sizeof(float) * (size_t)kvd);
-    or_attention(s->att, s->q, kl, vl, pos + 1, d, c->n_heads, m->kvh);
+    or_attention(s->att, s->q, kl + (size_t)lo * kvd, vl + (size_t)lo * kvd, pos - lo + 1, d,
+                 c->n_heads, m->kvh);
     or_matvec(s->t, m->wo[l], s->att, d, d);
     or_residual_add(s->x, s->t, d);
     ffn_block(m, l, s->x, s->xn, s->h1, s->h3, s->g, s->t);
@@ -381,7 +422,7 @@ int or_forward(const or_model* m, or_state* s, int token, int pos, float* logits
 
 int or_forward_recompute(const or_model* m, const int* tokens, int n, float* logits) {
   const or_config* c = &m->c;
-  if (n <= 0 || n > c->max_seq) return -2;
+  if (n <= 0 || n > max_pos(c)) return -2;
   for (int i = 0; i < n; ++i)
     if (tokens[i] < 0 || tokens[i] >= c->vocab_size) return -2;
   size_t d = (size_t)c->dim, f = (size_t)c->hidden_dim, kvd = (size_t)m->kvd;
@@ -410,13 +451,15 @@ int or_forward_recompute(const or_model* m, const int* tokens, int n, float* log
       or_rope(K + (size_t)i * kvd, (int)kvd, hd, m->rope_cos + (size_t)i * half,
               m->rope_sin + (size_t)i * half);
     }
-    /* then each position attends to positions 0..i */
+    /* then each position i attends to positions lo .. i of the window */
     for (int i = 0; i < n; ++i) {
       float* x = X + (size_t)i * d;
+      int lo = i - c->max_seq + 1 > 0 ? i - c->max_seq + 1 : 0;
       or_rmsnorm(xn, x, m->att_gain[l], (int)d, c->norm_eps);
       or_matvec(q, m->wq[l], xn, (int)d, (int)d);
       or_rope(q, (int)d, hd, m->rope_cos + (size_t)i * half, m->rope_sin + (size_t)i * half);
-      or_attention(att, q, K, Vv, i + 1, (int)d, c->n_heads, m->kvh);
+      or_attention(att, q, K + (size_t)lo * kvd, Vv + (size_t)lo * kvd, i - lo + 1, (int)d,
+                   c->n_heads, m->kvh);
       or_matvec(t, m->wo[l], att, (int)d, (int)d);
       or_residual_add(x, t, (int)d);
       ffn_block(m, l, x, xn, h1, h3, g, t);

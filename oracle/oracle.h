@@ -23,9 +23,15 @@
 extern "C" {
 #endif
 
-/* n_kv_heads: key/value heads (grouped-query attention); 0 means n_heads. */
+/* n_kv_heads: key/value heads (grouped-query attention); 0 means n_heads.
+ * weight_bf16: every matrix holds the generator's draw rounded to bfloat16
+ *   (or_bf16_round); the arithmetic is unchanged.
+ * max_pos: positions the model may run through; 0 means max_seq.  Beyond
+ *   max_seq, position p attends to the max_seq positions p-max_seq+1 .. p
+ *   (sliding window); rotary angles use the absolute position. */
 typedef struct {
   int32_t dim, n_layers, n_heads, hidden_dim, vocab_size, max_seq, tied, n_kv_heads;
+  int32_t weight_bf16, max_pos;
   double rope_theta, norm_eps;
 } or_config;
 
@@ -43,6 +49,7 @@ void or_attention(float* out, const float* q, const float* k_rows, const float* 
 void or_swiglu(float* g, const float* h1, const float* h3, int n);
 void or_residual_add(float* x, const float* t, int n);
 int or_argmax(const float* v, int n);
+float or_bf16_round(float x);
 
 /* ---- whole model ---- */
 /* Weights drawn from synth (std 0.02, gains 1.0); nthreads only speeds up the
@@ -57,13 +64,14 @@ float* or_model_tensor(or_model* m, int64_t id, size_t* n);
 or_state* or_state_create(const or_model* m);
 void or_state_free(or_state* s);
 
-/* One position: token at position pos (0 <= pos < max_seq), KV cache of `s`
+/* One position: token at position pos (0 <= pos < max_pos), KV cache of `s`
  * holds positions 0..pos-1.  Writes vocab_size logits; returns the greedy token
  * (lowest index among maxima) or -1 if a logit is not finite, -2 on bad input. */
 int or_forward(const or_model* m, or_state* s, int token, int pos, float* logits);
 
 /* Brute force, no cache: recompute every layer for all n positions of `tokens`
- * and write the logits of the last position.  Same return convention. */
+ * (n <= max_pos) and write the logits of the last position.  Same return
+ * convention. */
 int or_forward_recompute(const or_model* m, const int* tokens, int n, float* logits);
 
 #ifdef __cplusplus

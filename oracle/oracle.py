@@ -21,8 +21,8 @@ I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 class OrConfig(C.Structure):
     _fields_ = [("dim", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
                 ("hidden_dim", C.c_int32), ("vocab_size", C.c_int32), ("max_seq", C.c_int32),
-                ("tied", C.c_int32), ("n_kv_heads", C.c_int32), ("rope_theta", C.c_double),
-                ("norm_eps", C.c_double)]
+                ("tied", C.c_int32), ("n_kv_heads", C.c_int32), ("weight_bf16", C.c_int32),
+                ("max_pos", C.c_int32), ("rope_theta", C.c_double), ("norm_eps", C.c_double)]
 
 
 def lib(path=None):
@@ -53,6 +53,8 @@ def _bind(L):
     L.or_residual_add.argtypes = [F32P, F32P, C.c_int]
     L.or_argmax.argtypes = [F32P, C.c_int]
     L.or_argmax.restype = C.c_int
+    L.or_bf16_round.argtypes = [C.c_float]
+    L.or_bf16_round.restype = C.c_float
     L.or_model_create.argtypes = [C.POINTER(OrConfig), C.c_uint64, C.c_int]
     L.or_model_create.restype = C.c_void_p
     L.or_model_free.argtypes = [C.c_void_p]
@@ -149,6 +151,17 @@ def argmax(v, L=None):
     return int(L.or_argmax(v, v.size))
 
 
+def bf16_round(x, L=None):
+    """Each element rounded to the nearest bfloat16 (ties to even), as float32."""
+    L = L or lib()
+    x = _f32(x)
+    out = np.empty_like(x)
+    flat, src = out.reshape(-1), x.reshape(-1)
+    for i in range(src.size):
+        flat[i] = L.or_bf16_round(float(src[i]))
+    return out
+
+
 def synth_normal(seed, stream, start, n, std=0.02, nthreads=1, L=None):
     L = L or lib()
     out = np.empty(n, np.float32)
@@ -171,7 +184,8 @@ class OracleModel:
     """One model instance: weights drawn from `seed` (std 0.02, gains 1.0).
 
     cfg is any object with attributes dim, n_layers, n_heads, hidden_dim,
-    vocab_size, max_seq, tied, rope_theta, norm_eps (and optionally n_kv_heads).
+    vocab_size, max_seq, tied, rope_theta, norm_eps (and optionally n_kv_heads,
+    weight_bf16, max_pos).
     """
 
     def __init__(self, cfg, seed, nthreads=8, L=None):
@@ -179,6 +193,8 @@ class OracleModel:
         self.cfg = cfg
         c = OrConfig(cfg.dim, cfg.n_layers, cfg.n_heads, cfg.hidden_dim, cfg.vocab_size,
                      cfg.max_seq, int(cfg.tied), int(getattr(cfg, "n_kv_heads", 0) or 0),
+                     int(bool(getattr(cfg, "weight_bf16", False))),
+                     int(getattr(cfg, "max_pos", 0) or 0),
                      float(cfg.rope_theta), float(cfg.norm_eps))
         self._h = self.L.or_model_create(C.byref(c), seed, nthreads)
         if not self._h:

@@ -33,8 +33,16 @@ MUTANTS = {
     "rope_frequency_exponent": ("-(2.0 * (double)i) / (double)head_dim", "-(double)i / (double)head_dim"),
     "rope_not_applied_to_k": ("    or_rope(s->k, kvd, hd,", "    if (0) or_rope(s->k, kvd, hd,"),
     "attention_scale_1_over_hd": ("dot / sqrt((double)hd)", "dot / (double)hd"),
-    "attention_excludes_current_position": ("or_attention(s->att, s->q, kl, vl, pos + 1,",
-                                            "or_attention(s->att, s->q, kl, vl, pos > 0 ? pos : 1,"),
+    "attention_excludes_current_position": ("vl + (size_t)lo * kvd, pos - lo + 1, d,",
+                                            "vl + (size_t)lo * kvd, pos - lo > 0 ? pos - lo : 1, d,"),
+    "window_one_too_wide": ("int lo = pos - c->max_seq + 1 > 0 ? pos - c->max_seq + 1 : 0;",
+                            "int lo = pos - c->max_seq > 0 ? pos - c->max_seq : 0;"),
+    "window_ignored": ("int lo = pos - c->max_seq + 1 > 0 ? pos - c->max_seq + 1 : 0;", "int lo = 0;"),
+    "recompute_window_one_too_narrow": ("int lo = i - c->max_seq + 1 > 0 ? i - c->max_seq + 1 : 0;",
+                                        "int lo = i - c->max_seq + 2 > 0 ? i - c->max_seq + 2 : 0;"),
+    "bf16_truncates": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
+    "bf16_ties_away_from_zero": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    "bf16_not_applied_to_weights": ("if (c->weight_bf16)\n    for", "if (0)\n    for"),
     "attention_v_head_offset": ("v_rows[(size_t)j * kvd + kv_off + i]", "v_rows[(size_t)j * kvd + i]"),
     "gqa_kv_head_modulo": ("const size_t kv_off = (size_t)(h / group) * hd;",
                            "const size_t kv_off = (size_t)(h % n_kv_heads) * hd;"),

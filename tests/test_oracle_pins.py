@@ -422,3 +422,171 @@ def test_gqa_weight_shapes_and_bad_head_counts():
     with pytest.raises(ValueError):
         O.OracleModel(ModelConfig(dim=64, n_layers=1, n_heads=4, hidden_dim=32, vocab_size=10,
                                   max_seq=4, n_kv_heads=3), 1)
+
+
+# ------------------------------------------------------ bfloat16 weights ----
+# bfloat16 is the upper half of an IEEE binary32: sign, 8 exponent bits, 7
+# fraction bits (Kalamkar et al. 2019, sec. 2); the weights are the fp32 draws
+# rounded to nearest, ties to even.  torch's CPU conversion (round to nearest
+# even) is the independent reference.
+def _torch_bf16(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def _bits(x):
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def test_bf16_round_matches_torch_on_every_kind_of_value():
+    r = _rng(41)
+    parts = [r.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)]   # any bit pattern
+    hi = r.integers(0, 2**16, 4000, dtype=np.uint64).astype(np.uint32) << 16
+    parts.append(hi | 0x8000)                      # exactly halfway, both parities of the kept bit
+    parts.append(hi | 0x7FFF)
+    parts.append(hi | 0x8001)
+    parts.append(np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7F7FFFFF, 0x00000001,
+                           0x007FFFFF, 0x3F808000, 0x3F818000], np.uint32))
+    u = np.concatenate(parts)
+    x = u.view(np.float32)
+    got, want = O.bf16_round(x), _torch_bf16(x)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(_bits(got)[~nan], _bits(want)[~nan])
+
+
+def test_bf16_round_hand_worked():
+    one = 1.0
+    cases = [
+        (one, one),
+        (one + 2**-8, one),                        # halfway, kept bit 0: stays
+        (one + 3 * 2**-8, one + 2**-6),            # halfway, kept bit 1: rounds up to even
+        (one + 2**-8 + 2**-20, one + 2**-7),       # just past halfway
+        (-(one + 2**-8), -one),
+        (3.4028234663852886e38, math.inf),         # largest float: past the largest bfloat16
+        (2.0**-149, 0.0),                          # smallest subnormal: below half a bf16 quantum
+    ]
+    for x, want in cases:
+        assert float(O.bf16_round(np.array([x], np.float32))[0]) == want, x
+    # 0.02 to the nearest multiple of its bfloat16 quantum 2^-13 (7 fraction bits, 2^-6 <= 0.02 < 2^-5)
+    x = float(np.float32(0.02))
+    q = 2.0**-13
+    assert float(O.bf16_round(np.array([x], np.float32))[0]) == round(x / q) * q
+
+
+BF = ModelConfig(dim=32, n_layers=2, n_heads=4, hidden_dim=48, vocab_size=61, max_seq=12,
+                 tied=False, weight_bf16=True)
+
+
+def test_bf16_model_weights_are_the_rounded_draws():
+    seed = 42
+    m = O.OracleModel(BF, seed)
+    L = BF.n_layers
+    changed = 0
+    for sid in [0] + list(range(1, 1 + 7 * L)) + [1 + 7 * L]:
+        w = m.tensor(sid)
+        draw = O.synth_normal(seed, sid, 0, w.size)
+        assert np.array_equal(_bits(w), _bits(_torch_bf16(draw))), sid
+        assert np.all(_bits(w) & 0xFFFF == 0), sid
+        assert np.all(np.abs(w - draw) <= np.abs(draw) * 2.0**-8), sid   # half a unit in the 8th bit
+        changed += int(np.count_nonzero(w != draw))
+    assert changed > 0
+    for g in range(2 * L + 1):
+        assert np.all(m.tensor(-1 - g) == 1.0)     # norm gains stay fp32 ones
+
+
+def test_bf16_model_is_the_fp32_model_with_rounded_weights():
+    """only storage changes: an fp32 model given the rounded weights computes the same logits"""
+    seed = 43
+    bm = O.OracleModel(BF, seed)
+    fm = O.OracleModel(ModelConfig(**{**BF.__dict__, "weight_bf16": False}), seed)
+    L = BF.n_layers
+    for sid in [0] + list(range(1, 1 + 7 * L)) + [1 + 7 * L]:
+        fm.tensor(sid)[:] = _torch_bf16(fm.tensor(sid))
+    toks = O.synth_prompt(seed, 0, BF.max_seq, 0, BF.vocab_size)
+    s1, s2 = bm.new_state(), fm.new_state()
+    for p in range(BF.max_seq):
+        r1, l1 = bm.forward(s1, int(toks[p]), p)
+        r2, l2 = fm.forward(s2, int(toks[p]), p)
+        assert r1 == r2 and np.array_equal(l1, l2), p
+
+
+# --------------------------------------------- decoding past max_seq ----
+# The KV cache holds max_seq positions; past that, position p attends to the
+# window p-max_seq+1 .. p (sliding-window attention: Longformer, Beltagy et al.
+# 2020, sec. 3.1; Mistral 7B, Jiang et al. 2023, sec. 2), rotary angles of the
+# absolute position.
+def _win(n_layers, W, P, seed_cfg=0):
+    return ModelConfig(dim=32, n_layers=n_layers, n_heads=4, hidden_dim=48, vocab_size=61,
+                       max_seq=W, max_pos=P, tied=True)
+
+
+def _run(m, toks, upto):
+    st = m.new_state()
+    out = []
+    for p in range(upto):
+        r, lg = m.forward(st, int(toks[p]), p)
+        assert r >= 0
+        out.append(lg.copy())
+    return np.stack(out)
+
+
+def test_window_is_inactive_before_max_seq():
+    seed, W, P = 44, 8, 30
+    a = O.OracleModel(_win(2, W, P), seed)
+    b = O.OracleModel(_win(2, P, 0), seed)          # no window: the cache holds every position
+    toks = O.synth_prompt(seed, 0, P, 0, 61)
+    la, lb = _run(a, toks, P), _run(b, toks, P)
+    assert np.array_equal(la[:W], lb[:W])
+    assert all(not np.array_equal(la[p], lb[p]) for p in range(W, P))
+
+
+@pytest.mark.parametrize("n_layers,W", [(1, 6), (2, 5), (3, 4)])
+def test_window_receptive_field_is_exact(n_layers, W):
+    """logits at p depend on the tokens at p - L(W-1) .. p and on no earlier one
+    (each layer reaches W-1 positions further back)"""
+    seed, P = 45, 26
+    m = O.OracleModel(_win(n_layers, W, P), seed)
+    toks = O.synth_prompt(seed, 0, P, 0, 61)
+    base = _run(m, toks, P)
+    p = P - 1
+    edge = p - n_layers * (W - 1)
+    assert edge >= 1
+    for q, same in ((edge - 1, True), (edge, False)):
+        t2 = toks.copy()
+        t2[q] = (t2[q] + 1) % 61
+        lg = _run(m, t2, P)
+        assert np.array_equal(lg[p], base[p]) == same, q
+        assert np.array_equal(lg[:q], base[:q])       # causality
+
+
+def test_window_depends_on_relative_positions_only():
+    """one layer: the logits at p >= W equal those at W-1 of the same W tokens
+    started at position 0 (rotary scores depend on p - j; fp32 rounding of the
+    rotations at other absolute angles is the only difference)"""
+    seed, W, P = 46, 7, 24
+    m = O.OracleModel(_win(1, W, P), seed)
+    toks = O.synth_prompt(seed, 0, P, 0, 61)
+    lg = _run(m, toks, P)
+    for p in range(W, P):
+        ref = _run(m, toks[p - W + 1: p + 1], W)[-1]
+        assert np.allclose(lg[p], ref, rtol=1e-5, atol=1e-6), p
+
+
+def test_window_incremental_cache_equals_full_recomputation():
+    seed, W, P = 47, 5, 17
+    m = O.OracleModel(_win(2, W, P), seed)
+    toks = O.synth_prompt(seed, 0, P, 0, 61)
+    st = m.new_state()
+    for p in range(P):
+        r, lg = m.forward(st, int(toks[p]), p)
+        r2, lg2 = m.recompute(toks[: p + 1])
+        assert r == r2 and np.array_equal(lg, lg2), p
+
+
+def test_window_bounds():
+    m = O.OracleModel(_win(1, 4, 9), 1)
+    st = m.new_state()
+    assert m.forward(st, 0, 9)[0] == -2               # past max_pos
+    with pytest.raises(ValueError):
+        O.OracleModel(_win(1, 8, 5), 1)                # max_pos below max_seq

@@ -25,6 +25,9 @@ class ModelConfig:
     norm_eps: float = 1e-5
     max_batch: int = 1
     n_kv_heads: int = 0          # key/value heads (grouped-query attention); 0 = n_heads
+    weight_bf16: bool = False    # matrices held as bfloat16 (the fp32 draw rounded to nearest)
+    max_pos: int = 0             # positions the model may run through; 0 = max_seq.  Past
+                                 # max_seq, attention covers the max_seq most recent positions
 
     @property
     def head_dim(self):
@@ -43,10 +46,19 @@ class ModelConfig:
         per_layer = 2 * d * d + 2 * self.kv_dim * d + 3 * d * f + 2 * d
         return V * d + L * per_layer + d + (0 if self.tied else V * d)
 
+    @property
+    def weight_elem_bytes(self):
+        return 2 if self.weight_bf16 else 4
+
+    @property
+    def positions(self):
+        """positions the model may run through"""
+        return self.max_pos or self.max_seq
+
     def weight_bytes(self):
-        """fp32 bytes of every matrix the decode step streams once per token."""
+        """bytes of every matrix the decode step streams once per token."""
         d, f, V, L = self.dim, self.hidden_dim, self.vocab_size, self.n_layers
-        return 4 * (L * (2 * d * d + 2 * self.kv_dim * d + 3 * d * f) + V * d)
+        return self.weight_elem_bytes * (L * (2 * d * d + 2 * self.kv_dim * d + 3 * d * f) + V * d)
 
 
 @dataclass(frozen=True)

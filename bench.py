@@ -39,7 +39,7 @@ def step_bytes(cfg, pos, batch=1):
     once, plus per sequence the embedding row, norm gains, the K/V history read
     (positions 0..pos), the new K/V written and the logits written."""
     d, f, V, L, kvd = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers, cfg.kv_dim
-    weights = 4 * (L * (2 * d * d + 2 * kvd * d + 3 * d * f) + V * d)
+    weights = cfg.weight_elem_bytes * (L * (2 * d * d + 2 * kvd * d + 3 * d * f) + V * d)
     gains = 4 * (2 * L + 1) * d
     per_seq = 4 * (d + 2 * L * (pos + 1) * kvd + 2 * L * kvd + V)
     return weights + gains + batch * per_seq
@@ -47,9 +47,10 @@ def step_bytes(cfg, pos, batch=1):
 
 def w13_launch_bytes(cfg):
     """Algorithmic bytes of one W1/W3 + SwiGLU launch at batch 1: both weight
-    matrices once, the input row and its gain read, the gate row written."""
+    matrices once (4 or 2 bytes per element), the input row and its gain read,
+    the gate row written."""
     d, f = cfg.dim, cfg.hidden_dim
-    return 4 * (2 * f * d + 2 * d + f)
+    return cfg.weight_elem_bytes * 2 * f * d + 4 * (2 * d + f)
 
 
 def sources_hash(paths):
@@ -287,7 +288,8 @@ def main():
         achieved = w13_bytes / (w13_ms * 1e-3) / 1e9 if w13_ms > 0 else None
         roof = {
             "bound": "hbm",
-            "kernel": "W1/W3 + SwiGLU GEMV (k_gemv<EPI_SWIGLU>), batch 1",
+            "kernel": "W1/W3 + SwiGLU GEMV (k_gemv<EPI_SWIGLU>), batch 1%s"
+                      % (", bfloat16 weights" if cfg.weight_bf16 else ""),
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -334,7 +336,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",   # arithmetic; bfloat16 weights (when configured) are widened exactly
         "data": "synthetic",
         "config": {
             "workload": "%s: %s" % (w.name, w.description),
@@ -342,6 +344,7 @@ def main():
             "positions": "%d..%d" % (P, P + steps - 1),
             "prompt_tokens": int(prompt.shape[1]) if w.prompt_len else 0,
             "seed": w.model_seed,
+            "weights": "bf16" if cfg.weight_bf16 else "f32",
             "loop": ("ld_generate: one HIP graph replay per position" if args.graph else
                      "ld_decode_step per position, tokens fed back on the device"),
         },

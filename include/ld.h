@@ -26,7 +26,8 @@
  *    Output buffers (logits, next tokens) are caller-owned device memory.
  *  - All sequences of a batch share one position counter (lockstep decoding).
  *  - A handle is not thread-safe; separate handles are independent.
- *  - Tensors are fp32, token ids int32, matrices row-major [out][in].
+ *  - Tensors are fp32 (matrices optionally bfloat16, see weight_bf16), token
+ *    ids int32, matrices row-major [out][in].
  */
 #ifndef LD_H
 #define LD_H
@@ -61,6 +62,17 @@ typedef struct {
                               2023, sec. 2.2); 1 is multi-query attention, the pages'
                               TODO (openai.wiki "llama2.c | Baby LLaMA", "Unsorted TODO").
                               Wk and Wv are then [n_kv_heads * head_dim][dim]. */
+  int32_t weight_bf16;     /* 0: matrices held in fp32.  1: every matrix (embedding, Wq, Wk,
+                              Wv, Wo, W1, W2, W3, untied classifier) held as bfloat16, the
+                              upper half of an fp32 (Kalamkar et al. 2019, sec. 2), each
+                              element the generator's fp32 draw rounded to the nearest
+                              bfloat16, ties to even.  Only storage changes: every product
+                              is the exact product of the widened weight and the fp32
+                              activation, accumulated as in the fp32 model; norm gains,
+                              activations, KV cache and logits stay fp32.  The pages'
+                              engine is fp32 only (openai.wiki "llama2.c | Baby LLaMA",
+                              intro; Xinzhiyuan's llama2.c report, intro); this halves the
+                              bytes a decode step streams. */
   double rope_theta;       /* rotary base, 10000 for Llama-2 */
   double norm_eps;         /* RMSNorm epsilon, added inside the square root */
 } ld_config;
@@ -127,7 +139,8 @@ int ld_set_pos(ld_model* m, int32_t new_pos);
 int ld_get_pos(const ld_model* m, int32_t* pos);
 
 /* Copy elements [start, start+n) of weight tensor `stream_id` (synth stream
- * numbering, logical row-major layout) to host memory.  Synchronous. */
+ * numbering, logical row-major layout) to host memory as fp32 (bfloat16
+ * weights widened exactly).  Synchronous. */
 int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, float* host_out);
 
 /* Wait for the stream and report a device-side error raised since the last

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from transformer_llama_decode_amd.configs import TINY, TINY_UNTIED, SMALL, TINY_GQA, SMALL_MQA, ModelConfig
+from transformer_llama_decode_amd.configs import (TINY, TINY_UNTIED, SMALL, TINY_GQA, SMALL_MQA,
+                                                   TINY_BF16, SMALL_BF16, ModelConfig)
 from tests.parity import assert_logits, assert_token
 
 pytestmark = pytest.mark.gpu
@@ -60,6 +61,8 @@ CASES = [
     (TINY_GQA, 17, 1),
     (TINY_GQA, 17, 5),
     (SMALL_MQA, 18, 3),
+    (TINY_BF16, 25, 1),
+    (SMALL_BF16, 26, 4),
 ]
 
 

@@ -12,7 +12,7 @@ import pytest
 
 from oracle import oracle as O
 from transformer_llama_decode_amd.configs import (TINY, TINY_UNTIED, SMALL, TINY_GQA, SMALL_MQA,
-                                                   GQA_HD64, ModelConfig)
+                                                   GQA_HD64, TINY_BF16, SMALL_BF16, ModelConfig)
 from tests.parity import assert_logits, assert_token
 
 pytestmark = pytest.mark.gpu
@@ -62,13 +62,19 @@ CASES = [
     (TINY_GQA, 17),
     (SMALL_MQA, 18),
     (GQA_HD64, 19),
+    # bfloat16 weights
+    (TINY_BF16, 23),
+    (SMALL_BF16, 24),
 ]
 
 
 @pytest.mark.parametrize("cfg,seed", CASES)
 def test_weights_on_device_are_the_generator_values(dev, cfg, seed):
+    """bit-identical to the oracle's weights: the generator's draws, for bfloat16
+    weights rounded to nearest even (the library rounds by scaling on the host,
+    the oracle on the bit pattern)"""
     _say("weights", cfg)
-    gm, _ = _models(cfg, seed)
+    gm, om = _models(cfg, seed)
     L = cfg.n_layers
     ids = [0] + list(range(1, 1 + 7 * L)) + ([] if cfg.tied else [1 + 7 * L])
     for sid in ids:
@@ -79,8 +85,11 @@ def test_weights_on_device_are_the_generator_values(dev, cfg, seed):
             n = cfg.dim * (cfg.hidden_dim if kind in (4, 5, 6) else
                            cfg.kv_dim if kind in (1, 2) else cfg.dim)
         got = gm.read_weights(sid, 0, n)
-        want = O.synth_normal(seed, sid, 0, n)
-        assert np.array_equal(got, want), sid
+        want = om.tensor(sid)
+        assert want.size == n
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), sid
+        if not cfg.weight_bf16:
+            assert np.array_equal(want, O.synth_normal(seed, sid, 0, n)), sid
     gm.close()
 
 
@@ -164,7 +173,7 @@ def test_batched_lockstep_matches_each_sequence_alone(dev, cfg, seed):
     gm.close()
 
 
-@pytest.mark.parametrize("cfg,seed", [(TINY, 11), (SMALL, 12), (SMALL_MQA, 13)])
+@pytest.mark.parametrize("cfg,seed", [(TINY, 11), (SMALL, 12), (SMALL_MQA, 13), (SMALL_BF16, 14)])
 def test_many_row_prefill_every_logit(dev, cfg, seed):
     # more than 256 rows per forward pass: the LDS-tiled MFMA GEMM path
     # (smaller row counts take the split-K path exercised above)
@@ -277,6 +286,9 @@ LONG = [
                  max_batch=2), 43),
     (ModelConfig(dim=256, n_layers=2, n_heads=2, hidden_dim=192, vocab_size=1001, max_seq=330,
                  max_batch=2, n_kv_heads=1), 44),
+    # bfloat16 weights, grouped-query
+    (ModelConfig(dim=256, n_layers=2, n_heads=4, hidden_dim=192, vocab_size=1001, max_seq=330,
+                 max_batch=2, n_kv_heads=2, weight_bf16=True), 46),
     # head dim 48: not a multiple of 32, rows share K/V tiles on the vector units
     (ModelConfig(dim=192, n_layers=2, n_heads=4, hidden_dim=160, vocab_size=1001, max_seq=330,
                  max_batch=2), 45),
@@ -314,7 +326,7 @@ def test_long_prompt_prefill_every_logit(dev, cfg, seed):
     gm.close()
 
 
-@pytest.mark.parametrize("cfg,seed", [LONG[1], LONG[3]])
+@pytest.mark.parametrize("cfg,seed", [LONG[1], LONG[3], LONG[4]])
 def test_prompt_in_two_pieces_every_logit(dev, cfg, seed):
     """a prompt fed as 100 + 201 tokens: the second piece attends to the first
     piece's cache entries at positions below its own rows"""

@@ -65,17 +65,22 @@ def _cfg(m, **kw):
 @pytest.mark.parametrize("bad", [dict(dim=100), dict(n_heads=5), dict(hidden_dim=100), dict(vocab_size=0),
                                  dict(max_seq=0), dict(max_batch=0), dict(rope_theta=0.0),
                                  dict(dim=64, n_heads=1, hidden_dim=64, vocab_size=10, max_seq=4) | {"n_layers": 0},
-                                 dict(dim=512, n_heads=1), dict(n_kv_heads=3), dict(n_kv_heads=-1)])
+                                 dict(dim=512, n_heads=1), dict(n_kv_heads=3), dict(n_kv_heads=-1),
+                                 dict(weight_bf16=2)])
 def test_arena_bytes_rejects_unsupported_configs(L, bad):
     n = C.c_size_t(0)
-    assert L.ld_arena_bytes(C.byref(_cfg(TINY, **bad)), C.byref(n)) == _lib.LD_E_INVAL
+    raw = {k: bad.pop(k) for k in list(bad) if k == "weight_bf16"}   # set on the C struct as is
+    c = _cfg(TINY, **bad)
+    for k, v in raw.items():
+        setattr(c, k, v)
+    assert L.ld_arena_bytes(C.byref(c), C.byref(n)) == _lib.LD_E_INVAL
 
 
 def test_arena_sizes_of_the_workloads(L):
     for name, w in WORKLOADS.items():
         n = C.c_size_t(0)
         assert L.ld_arena_bytes(C.byref(_cfg(w.model)), C.byref(n)) == 0
-        weights = w.model.n_params() * 4
+        weights = w.model.n_params() * w.model.weight_elem_bytes
         assert weights <= n.value < weights * 1.3 + 3 * 2 ** 30, name
     n = C.c_size_t(0)
     L.ld_arena_bytes(C.byref(_cfg(WORKLOADS["C5"].model)), C.byref(n))
@@ -112,3 +117,15 @@ def test_grouped_query_arena_saves_the_key_value_rows_and_cache(L):
     for kvh in (2, 1):
         saved = 4 * Lr * (2 * (d - kvh * hd) * d + 2 * B * S * (d - kvh * hd))
         assert abs((sizes[0] - sizes[kvh]) - saved) <= 8 * 256, kvh
+
+
+def test_bfloat16_arena_halves_the_matrices(L):
+    from dataclasses import replace
+    for tied in (True, False):
+        m = ModelConfig(dim=256, n_layers=3, n_heads=8, hidden_dim=320, vocab_size=301, max_seq=64,
+                        max_batch=2, tied=tied)
+        n32, n16 = C.c_size_t(0), C.c_size_t(0)
+        assert L.ld_arena_bytes(C.byref(_cfg(m)), C.byref(n32)) == 0
+        assert L.ld_arena_bytes(C.byref(_cfg(replace(m, weight_bf16=True))), C.byref(n16)) == 0
+        matrices = m.n_params() - (2 * m.n_layers + 1) * m.dim      # all but the norm gains
+        assert abs((n32.value - n16.value) - 2 * matrices) <= 16 * 256, tied

@@ -104,6 +104,11 @@ WORKLOADS = {
     "C5": Workload("C5", M7B, 4, 1, 512, 4, 1024,
                    description="7B shape (4096/32L/32H, 11008 hidden), b1, 512-token prompt, "
                                "512 decode steps"),
+    # the 7B shape with bfloat16 weights (fp32 activations and arithmetic): half the
+    # bytes per step
+    "C5bf16": Workload("C5bf16", replace(M7B, weight_bf16=True), 4, 1, 512, 4, 1024,
+                       description="7B shape, bfloat16 weights, b1, 512-token prompt, "
+                                   "512 decode steps"),
     # grouped-query variant of the 7B shape: 8 key/value heads shared by groups of 4
     # query heads (a measurement of the grouped-query row; not one of the five configs)
     "C5g8": Workload("C5g8", replace(M7B, n_kv_heads=8), 4, 1, 512, 4, 1024,
@@ -124,3 +129,7 @@ SMALL_MQA = ModelConfig(dim=128, n_layers=3, n_heads=4, hidden_dim=352, vocab_si
                         max_seq=160, max_batch=7, n_kv_heads=1)
 GQA_HD64 = ModelConfig(dim=256, n_layers=2, n_heads=4, hidden_dim=320, vocab_size=2011,
                        max_seq=200, max_batch=4, n_kv_heads=2)
+# bfloat16 weights: untied classifier (head dim 32), and tied (the classifier
+# reads the bfloat16 embedding table)
+TINY_BF16 = replace(TINY_UNTIED, weight_bf16=True)
+SMALL_BF16 = replace(SMALL, weight_bf16=True)

@@ -50,6 +50,15 @@ __device__ __forceinline__ double dot4(const float4 w, double x0, double x1, dou
   return acc;
 }
 
+// bfloat16 is the upper half of an fp32, so widening one is a 16-bit shift
+// (exact).  A 32-bit word holds two: element 2i in the low half (little endian).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+// four consecutive bfloat16 (8 bytes) as four floats
+__device__ __forceinline__ float4 bf16x4(const uint2 u) {
+  return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+}
+
 // SwiGLU gate in double, rounded once: silu(h1) * h3, silu(z) = z / (1 + e^-z).
 __device__ __forceinline__ float swiglu(float h1, float h3) {
   double z = (double)h1;

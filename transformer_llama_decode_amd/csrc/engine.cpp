@@ -46,6 +46,7 @@ int validate(const ld_config* c) {
   if (c->max_seq <= 0 || c->max_seq > (1 << 16)) return LD_E_INVAL;
   if (c->max_batch <= 0 || c->max_batch > 4096) return LD_E_INVAL;
   if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0)) return LD_E_INVAL;
+  if (c->weight_bf16 != 0 && c->weight_bf16 != 1) return LD_E_INVAL;
   return LD_OK;
 }
 
@@ -54,22 +55,23 @@ void make_layout(const ld_config* c, Layout* L) {
                H = c->n_heads, hd = d / H, S = c->max_seq, B = c->max_batch;
   const size_t kvd = (size_t)kv_heads(c) * hd;   // rows of Wk and of Wv
   const size_t Sp = round_up(S, 64);
+  const size_t es = c->weight_bf16 ? 2 : 4;       // bytes per matrix element
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off += round_up(bytes, kAlign);
     return o;
   };
-  L->E = take(V * d * 4);
+  L->E = take(V * d * es);
   L->o_wqkv = 0;
-  L->o_wo = L->o_wqkv + round_up((d + 2 * kvd) * d * 4, kAlign);
-  L->o_w13 = L->o_wo + round_up(d * d * 4, kAlign);
-  L->o_w2 = L->o_w13 + round_up(2 * f * d * 4, kAlign);
-  L->o_gatt = L->o_w2 + round_up(d * f * 4, kAlign);
+  L->o_wo = L->o_wqkv + round_up((d + 2 * kvd) * d * es, kAlign);
+  L->o_w13 = L->o_wo + round_up(d * d * es, kAlign);
+  L->o_w2 = L->o_w13 + round_up(2 * f * d * es, kAlign);
+  L->o_gatt = L->o_w2 + round_up(d * f * es, kAlign);
   L->o_gffn = L->o_gatt + round_up(d * 4, kAlign);
   L->layer_stride = L->o_gffn + round_up(d * 4, kAlign);
   L->layer0 = take(L->layer_stride * NL);
-  L->Wcls = c->tied_classifier ? L->E : take(V * d * 4);
+  L->Wcls = c->tied_classifier ? L->E : take(V * d * es);
   L->gain_final = take(d * 4);
   L->rope_cos = take(S * (hd / 2) * 4);
   L->rope_sin = take(S * (hd / 2) * 4);
@@ -114,6 +116,8 @@ struct ld_model {
   char* arena;
   int pos;
   bool carry;
+  bool bf16;             // matrices held as bfloat16
+  size_t wes;            // bytes per matrix element (4 or 2)
   bool stream_weights;   // weights exceed the Infinity Cache: stream them non-temporally
   int* tok_host[kTokSlots];
   hipEvent_t tok_ev[kTokSlots];
@@ -130,6 +134,10 @@ struct ld_model {
   template <typename T>
   T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
   float* layer(int l, size_t o) const { return at<float>(lay.layer0 + (size_t)l * lay.layer_stride + o); }
+  // matrix region `o` of layer l, advanced by `elems` matrix elements
+  char* wlayer(int l, size_t o, size_t elems = 0) const {
+    return arena + lay.layer0 + (size_t)l * lay.layer_stride + o + elems * wes;
+  }
   float* kc(int l) const {
     return at<float>(lay.Kc) + (size_t)l * c.max_batch * kvh * lay.seq_pad * hd;
   }
@@ -188,29 +196,54 @@ int host_threads() {
   return n;
 }
 
+// fp32 -> bfloat16 (the upper 16 bits of the fp32 pattern), rounded to
+// nearest with ties to even: the value is scaled so that bfloat16's quantum
+// at its binade (8 significant bits; 2^-133 below the normal range) becomes 1,
+// rounded to an integer by nearbyint (the default mode rounds half to even),
+// and scaled back -- all exact in double.  The generator draws finite values.
+uint16_t to_bf16(float w) {
+  double q = 0.0;
+  if (w != 0.0f) {
+    int e;
+    std::frexp((double)w, &e);   // |w| = m 2^e, 0.5 <= m < 1
+    q = std::ldexp(1.0, std::max(e - 8, -133));
+  }
+  const float r = q == 0.0 ? w : (float)(std::nearbyint((double)w / q) * q);
+  uint32_t u;
+  std::memcpy(&u, &r, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
 // One piece of host-side weight drawing: n elements of stream `stream`
-// starting at `start` into dst.
+// starting at `start` into dst (fp32, or bfloat16 when bf16).
 struct Seg {
-  float* dst;
+  void* dst;
   uint64_t stream, start;
   size_t n;
 };
 
-void draw_segments(const std::vector<Seg>& segs, uint64_t seed, int nthreads) {
+void draw_segments(const std::vector<Seg>& segs, uint64_t seed, int nthreads, bool bf16) {
   // split into pieces of >= 64K elements and hand them out dynamically
+  const size_t piece = 1 << 16, es = bf16 ? 2 : 4;
   std::vector<Seg> pieces;
   for (const Seg& s : segs) {
-    const size_t piece = 1 << 16;
     for (size_t o = 0; o < s.n; o += piece)
-      pieces.push_back({s.dst + o, s.stream, s.start + o, std::min(piece, s.n - o)});
+      pieces.push_back({static_cast<char*>(s.dst) + o * es, s.stream, s.start + o, std::min(piece, s.n - o)});
   }
   std::atomic<size_t> next{0};
   auto work = [&]() {
+    std::vector<float> tmp(bf16 ? piece : 0);
     for (;;) {
       size_t i = next.fetch_add(1);
       if (i >= pieces.size()) return;
       const Seg& p = pieces[i];
-      synth_normal(p.dst, seed, p.stream, p.start, p.n, 0.02);
+      if (!bf16) {
+        synth_normal(static_cast<float*>(p.dst), seed, p.stream, p.start, p.n, 0.02);
+        continue;
+      }
+      synth_normal(tmp.data(), seed, p.stream, p.start, p.n, 0.02);
+      uint16_t* o = static_cast<uint16_t*>(p.dst);
+      for (size_t k = 0; k < p.n; ++k) o[k] = to_bf16(tmp[k]);
     }
   };
   std::vector<std::thread> th;
@@ -224,7 +257,8 @@ struct Uploader {
   hipStream_t s;
   uint64_t seed;
   int nthreads;
-  size_t cap;   // floats per staging buffer
+  bool bf16;    // matrices are held as bfloat16
+  size_t cap;   // elements per staging buffer (sized for fp32)
   float* stage[2] = {nullptr, nullptr};
   hipEvent_t ev[2];
   bool live[2] = {false, false};
@@ -248,42 +282,44 @@ struct Uploader {
       }
     }
   }
-  float* acquire() {
+  void* acquire() {
     if (live[cur]) {
       if (hipEventSynchronize(ev[cur]) != hipSuccess) ok = false;
       live[cur] = false;
     }
     return stage[cur];
   }
-  void submit(void* dev, size_t nfloats) {
-    if (hipMemcpyAsync(dev, stage[cur], nfloats * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
+  void submit(void* dev, size_t nelems) {
+    if (hipMemcpyAsync(dev, stage[cur], nelems * (bf16 ? 2 : 4), hipMemcpyHostToDevice, s) != hipSuccess ||
         hipEventRecord(ev[cur], s) != hipSuccess)
       ok = false;
     live[cur] = true;
     cur ^= 1;
   }
+  // elements `o` on from `p`, in the matrices' element size
+  char* adv(void* p, size_t o) const { return static_cast<char*>(p) + o * (bf16 ? 2 : 4); }
   // plain row-major tensor
-  void plain(float* dev, uint64_t stream, size_t n) {
+  void plain(void* dev, uint64_t stream, size_t n) {
     for (size_t o = 0; o < n && ok; o += cap) {
       const size_t cnt = std::min(cap, n - o);
-      float* h = acquire();
-      draw_segments({{h, stream, o, cnt}}, seed, nthreads);
-      submit(dev + o, cnt);
+      void* h = acquire();
+      draw_segments({{h, stream, o, cnt}}, seed, nthreads, bf16);
+      submit(adv(dev, o), cnt);
     }
   }
   // W1 (stream s1) and W3 (stream s3), f rows of d each, interleaved in 32-row blocks
-  void w13(float* dev, uint64_t s1, uint64_t s3, size_t f, size_t d) {
+  void w13(void* dev, uint64_t s1, uint64_t s3, size_t f, size_t d) {
     size_t rows_per = std::max<size_t>(32, (cap / (2 * d)) / 32 * 32);
     for (size_t r0 = 0; r0 < f && ok; r0 += rows_per) {
       const size_t nr = std::min(rows_per, f - r0);   // multiple of 32
-      float* h = acquire();
+      void* h = acquire();
       std::vector<Seg> segs;
       for (size_t j = 0; j < nr / 32; ++j) {
-        segs.push_back({h + (2 * j) * 32 * d, s1, (r0 + 32 * j) * d, 32 * d});
-        segs.push_back({h + (2 * j + 1) * 32 * d, s3, (r0 + 32 * j) * d, 32 * d});
+        segs.push_back({adv(h, (2 * j) * 32 * d), s1, (r0 + 32 * j) * d, 32 * d});
+        segs.push_back({adv(h, (2 * j + 1) * 32 * d), s3, (r0 + 32 * j) * d, 32 * d});
       }
-      draw_segments(segs, seed, nthreads);
-      submit(dev + 2 * r0 * d, 2 * nr * d);
+      draw_segments(segs, seed, nthreads, bf16);
+      submit(adv(dev, 2 * r0 * d), 2 * nr * d);
     }
   }
 };
@@ -320,7 +356,8 @@ int layers_gemv(ld_model* m, int pos) {
       GemvArgs a{};
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = x; a.gain = m->layer(l, m->lay.o_gatt); a.eps = c.norm_eps;
-      a.W = m->layer(l, m->lay.o_wqkv); a.N = d + 2 * m->kvd; a.K = d; a.stream = m->stream_weights;
+      a.W = m->wlayer(l, m->lay.o_wqkv); a.bf16 = m->bf16; a.N = d + 2 * m->kvd; a.K = d;
+      a.stream = m->stream_weights;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
       a.pos = pos; a.d = d; a.hd = m->hd; a.seq_pad = m->lay.seq_pad; a.pos_dev = pos_dev;
@@ -340,7 +377,7 @@ int layers_gemv(ld_model* m, int pos) {
       ProfScope ps(m, K_WO, true);
       GemvArgs a{};
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.x = att; a.W = m->layer(l, m->lay.o_wo); a.N = d; a.K = d; a.resid = x;
+      a.x = att; a.W = m->wlayer(l, m->lay.o_wo); a.bf16 = m->bf16; a.N = d; a.K = d; a.resid = x;
       a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_resid(a, m->stream));
     }
@@ -349,7 +386,7 @@ int layers_gemv(ld_model* m, int pos) {
       GemvArgs a{};
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.x = x; a.gain = m->layer(l, m->lay.o_gffn); a.eps = c.norm_eps;
-      a.W = m->layer(l, m->lay.o_w13); a.N = f; a.K = d; a.g_out = g;
+      a.W = m->wlayer(l, m->lay.o_w13); a.bf16 = m->bf16; a.N = f; a.K = d; a.g_out = g;
       a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_swiglu(a, m->stream));
     }
@@ -357,7 +394,7 @@ int layers_gemv(ld_model* m, int pos) {
       ProfScope ps(m, K_W2, true);
       GemvArgs a{};
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.x = g; a.W = m->layer(l, m->lay.o_w2); a.N = d; a.K = f; a.resid = x;
+      a.x = g; a.W = m->wlayer(l, m->lay.o_w2); a.bf16 = m->bf16; a.N = d; a.K = f; a.resid = x;
       a.stream = m->stream_weights;
       LD_TRY_HIP(launch_gemv_resid(a, m->stream));
     }
@@ -383,7 +420,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = xn; a.W = m->layer(l, m->lay.o_wqkv); a.M = rows; a.N = d + 2 * m->kvd; a.K = d;
+      a.A = xn; a.W = m->wlayer(l, m->lay.o_wqkv); a.bf16 = m->bf16; a.M = rows; a.N = d + 2 * m->kvd; a.K = d;
       a.carry = m->carry; a.kvh = m->kvh;
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
@@ -405,7 +442,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = att; a.W = m->layer(l, m->lay.o_wo); a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
+      a.A = att; a.W = m->wlayer(l, m->lay.o_wo); a.bf16 = m->bf16; a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
       a.resid = x;
       LD_TRY_HIP(launch_gemm_resid(a, m->stream));
     }
@@ -416,7 +453,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = xn; a.W = m->layer(l, m->lay.o_w13); a.M = rows; a.N = 2 * f; a.K = d; a.carry = m->carry;
+      a.A = xn; a.W = m->wlayer(l, m->lay.o_w13); a.bf16 = m->bf16; a.M = rows; a.N = 2 * f; a.K = d; a.carry = m->carry;
       a.g_out = g; a.f = f;
       LD_TRY_HIP(launch_gemm_swiglu(a, m->stream));
     }
@@ -425,7 +462,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = g; a.W = m->layer(l, m->lay.o_w2); a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
+      a.A = g; a.W = m->wlayer(l, m->lay.o_w2); a.bf16 = m->bf16; a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
       a.resid = x;
       LD_TRY_HIP(launch_gemm_resid(a, m->stream));
     }
@@ -455,7 +492,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
     GemvArgs a{};
     a.ev_start = ps.start(); a.ev_stop = ps.stop();
     a.x = x + (size_t)(n_tok - 1) * d; a.gain = m->at<float>(m->lay.gain_final); a.eps = c.norm_eps;
-    a.W = m->at<float>(m->lay.Wcls); a.N = V; a.K = d; a.stream = m->stream_weights;
+    a.W = m->arena + m->lay.Wcls; a.bf16 = m->bf16; a.N = V; a.K = d; a.stream = m->stream_weights;
     a.logits = logits ? logits + (size_t)out_row0 * V : nullptr;
     a.part_val = pv; a.part_idx = pi; a.err = err;
     LD_TRY_HIP(launch_gemv_cls(a, &nparts, m->stream));
@@ -468,7 +505,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
                                      c.norm_eps, m->stream));
     GemmArgs a{};
     a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
-    a.A = xn; a.W = m->at<float>(m->lay.Wcls); a.M = cls_rows; a.N = V; a.K = d; a.carry = m->carry;
+    a.A = xn; a.W = m->arena + m->lay.Wcls; a.bf16 = m->bf16; a.M = cls_rows; a.N = V; a.K = d; a.carry = m->carry;
     a.logits = logits;
     a.n_tok = all_pos ? n_tok : 1;
     a.logit_rows_per_seq = all_pos ? out_rows_per_seq : 1;
@@ -513,7 +550,7 @@ int build_step_graph(ld_model* m, int batch, float* dev_logits) {
     rc = LD_E_HIP;
   } else {
     int* pd = m->at<int>(m->lay.pos_dev);
-    if (launch_embed(m->at<int>(m->lay.next), m->at<float>(m->lay.E), m->at<float>(m->lay.x), batch,
+    if (launch_embed(m->at<int>(m->lay.next), m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x), batch,
                      c.dim, c.vocab_size, m->at<int>(m->lay.err), pd + 1, pd, m->stream) != hipSuccess)
       rc = LD_E_HIP;
     if (rc == LD_OK) rc = (batch == 1) ? layers_gemv(m, 0) : layers_gemm(m, batch, 1, 0);
@@ -577,8 +614,10 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
   m->pos = 0;
   // fp32 MFMA sums are carried into fp64 for wide models (K >= 2048)
   m->carry = cfg->dim >= 2048;
+  m->bf16 = cfg->weight_bf16 == 1;
+  m->wes = m->bf16 ? 2 : 4;
   {
-    const size_t wbytes = 4 * ((size_t)cfg->n_layers * ((2 * (size_t)cfg->dim + 2 * (size_t)m->kvd) * cfg->dim +
+    const size_t wbytes = m->wes * ((size_t)cfg->n_layers * ((2 * (size_t)cfg->dim + 2 * (size_t)m->kvd) * cfg->dim +
                                                           3 * (size_t)cfg->dim * cfg->hidden_dim) +
                                (size_t)cfg->vocab_size * cfg->dim * (cfg->tied_classifier ? 1 : 2));
     m->stream_weights = wbytes > ((size_t)256 << 20);
@@ -617,25 +656,25 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
     Uploader up;
     up.s = m->stream;
     up.seed = seed;
+    up.bf16 = m->bf16;
     up.nthreads = host_threads();
     up.cap = (size_t)16 << 20;   // 64 MiB per staging buffer
     if (up.init() != LD_OK) return fail(LD_E_HIP);
-    up.plain(m->at<float>(L.E), synth_stream_embedding(), V * d);
+    up.plain(m->arena + L.E, synth_stream_embedding(), V * d);
     for (int l = 0; l < cfg->n_layers && up.ok; ++l) {
-      float* wqkv = m->layer(l, L.o_wqkv);
       const size_t kvd = (size_t)m->kvd;
-      up.plain(wqkv, synth_stream_layer(l, 0), d * d);
-      up.plain(wqkv + d * d, synth_stream_layer(l, 1), kvd * d);
-      up.plain(wqkv + d * d + kvd * d, synth_stream_layer(l, 2), kvd * d);
-      up.plain(m->layer(l, L.o_wo), synth_stream_layer(l, 3), d * d);
-      up.w13(m->layer(l, L.o_w13), synth_stream_layer(l, 4), synth_stream_layer(l, 6), f, d);
-      up.plain(m->layer(l, L.o_w2), synth_stream_layer(l, 5), d * f);
+      up.plain(m->wlayer(l, L.o_wqkv), synth_stream_layer(l, 0), d * d);
+      up.plain(m->wlayer(l, L.o_wqkv, d * d), synth_stream_layer(l, 1), kvd * d);
+      up.plain(m->wlayer(l, L.o_wqkv, d * d + kvd * d), synth_stream_layer(l, 2), kvd * d);
+      up.plain(m->wlayer(l, L.o_wo), synth_stream_layer(l, 3), d * d);
+      up.w13(m->wlayer(l, L.o_w13), synth_stream_layer(l, 4), synth_stream_layer(l, 6), f, d);
+      up.plain(m->wlayer(l, L.o_w2), synth_stream_layer(l, 5), d * f);
       if (launch_fill(m->layer(l, L.o_gatt), 1.0f, d, m->stream) != hipSuccess ||
           launch_fill(m->layer(l, L.o_gffn), 1.0f, d, m->stream) != hipSuccess)
         up.ok = false;
     }
     if (up.ok && !cfg->tied_classifier)
-      up.plain(m->at<float>(L.Wcls), synth_stream_classifier(cfg->n_layers), V * d);
+      up.plain(m->arena + L.Wcls, synth_stream_classifier(cfg->n_layers), V * d);
     if (!up.ok) return fail(LD_E_HIP);
     if (launch_fill(m->at<float>(L.gain_final), 1.0f, d, m->stream) != hipSuccess) return fail(LD_E_HIP);
     // rotary tables: angle p * theta^(-2i/hd), cos/sin in double, stored fp32
@@ -676,7 +715,7 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
     if (rc != LD_OK) return rc;
   }
   const ld_config& c = m->c;
-  LD_TRY_HIP(launch_embed(d_tok, m->at<float>(m->lay.E), m->at<float>(m->lay.x), batch, c.dim,
+  LD_TRY_HIP(launch_embed(d_tok, m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x), batch, c.dim,
                           c.vocab_size, m->at<int>(m->lay.err), nullptr, nullptr, m->stream));
   int rc = (batch == 1) ? layers_gemv(m, m->pos) : layers_gemm(m, batch, 1, m->pos);
   if (rc != LD_OK) return rc;
@@ -706,7 +745,7 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
                   sizeof(int32_t) * nc);
     int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows, m->at<int>(m->lay.tok));
     if (rc != LD_OK) return rc;
-    LD_TRY_HIP(launch_embed(m->at<int>(m->lay.tok), m->at<float>(m->lay.E), m->at<float>(m->lay.x),
+    LD_TRY_HIP(launch_embed(m->at<int>(m->lay.tok), m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x),
                             rows, c.dim, c.vocab_size, m->at<int>(m->lay.err), nullptr, nullptr,
                             m->stream));
     rc = (rows == 1) ? layers_gemv(m, pos0 + t0) : layers_gemm(m, rows, nc, pos0 + t0);
@@ -773,34 +812,38 @@ int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, 
   const ld_config& c = m->c;
   const uint64_t d = c.dim, f = c.hidden_dim, V = c.vocab_size, NL = c.n_layers;
   DeviceGuard dg(m->device);
-  const float* base = nullptr;
+  const char* base = nullptr;
   uint64_t total = 0;
   int kind = -1, layer = -1;
   if (stream_id == 0) {
-    base = m->at<float>(m->lay.E);
+    base = m->arena + m->lay.E;
     total = V * d;
   } else if (stream_id == (int64_t)(1 + 7 * NL)) {
     if (c.tied_classifier) return LD_E_INVAL;
-    base = m->at<float>(m->lay.Wcls);
+    base = m->arena + m->lay.Wcls;
     total = V * d;
   } else if (stream_id >= 1 && stream_id <= (int64_t)(7 * NL)) {
     layer = (int)((stream_id - 1) / 7);
     kind = (int)((stream_id - 1) % 7);
     switch (kind) {
-      case 0: base = m->layer(layer, m->lay.o_wqkv); total = d * d; break;
-      case 1: base = m->layer(layer, m->lay.o_wqkv) + d * d; total = (uint64_t)m->kvd * d; break;
+      case 0: base = m->wlayer(layer, m->lay.o_wqkv); total = d * d; break;
+      case 1: base = m->wlayer(layer, m->lay.o_wqkv, d * d); total = (uint64_t)m->kvd * d; break;
       case 2:
-        base = m->layer(layer, m->lay.o_wqkv) + d * d + (uint64_t)m->kvd * d;
+        base = m->wlayer(layer, m->lay.o_wqkv, d * d + (uint64_t)m->kvd * d);
         total = (uint64_t)m->kvd * d;
         break;
-      case 3: base = m->layer(layer, m->lay.o_wo); total = d * d; break;
-      case 5: base = m->layer(layer, m->lay.o_w2); total = d * f; break;
-      default: base = m->layer(layer, m->lay.o_w13); total = f * d; break;   // W1 (4), W3 (6)
+      case 3: base = m->wlayer(layer, m->lay.o_wo); total = d * d; break;
+      case 5: base = m->wlayer(layer, m->lay.o_w2); total = d * f; break;
+      default: base = m->wlayer(layer, m->lay.o_w13); total = f * d; break;   // W1 (4), W3 (6)
     }
   } else {
     return LD_E_INVAL;
   }
   if (start > total || n > total - start) return LD_E_RANGE;
+  const uint64_t es = m->wes;
+  // bfloat16 elements land in a host staging copy and are widened afterwards
+  std::vector<uint16_t> raw(m->bf16 ? n : 0);
+  char* dst = m->bf16 ? reinterpret_cast<char*>(raw.data()) : reinterpret_cast<char*>(host_out);
   if (kind == 4 || kind == 6) {
     // interleaved 32-row blocks: copy row pieces
     uint64_t i = start;
@@ -808,14 +851,18 @@ int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, 
       const uint64_t r = i / d, col = i % d;
       const uint64_t dev_row = (r / 32) * 64 + (r % 32) + (kind == 6 ? 32 : 0);
       const uint64_t cnt = std::min(d - col, start + n - i);
-      LD_TRY_HIP(hipMemcpyAsync(host_out + (i - start), base + dev_row * d + col, cnt * 4,
+      LD_TRY_HIP(hipMemcpyAsync(dst + (i - start) * es, base + (dev_row * d + col) * es, cnt * es,
                                 hipMemcpyDeviceToHost, m->stream));
       i += cnt;
     }
   } else {
-    LD_TRY_HIP(hipMemcpyAsync(host_out, base + start, n * 4, hipMemcpyDeviceToHost, m->stream));
+    LD_TRY_HIP(hipMemcpyAsync(dst, base + start * es, n * es, hipMemcpyDeviceToHost, m->stream));
   }
   LD_TRY_HIP(hipStreamSynchronize(m->stream));
+  for (uint64_t k = 0; k < raw.size(); ++k) {
+    const uint32_t u = (uint32_t)raw[k] << 16;
+    std::memcpy(host_out + k, &u, sizeof u);
+  }
   return LD_OK;
 }
 

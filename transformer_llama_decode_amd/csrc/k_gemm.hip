@@ -10,6 +10,8 @@
 //    of its A row and of its W row as one float4, and 4 MFMAs consume them.
 //    Each MFMA sums over 2 k (one per lane half); the k order inside a K step is
 //    a fixed permutation shared by A and W, so the product is unchanged;
+//  * bfloat16 weights are widened to fp32 (exactly) as they are loaded, so the
+//    LDS tiles and the matrix-core arithmetic are those of fp32 weights;
 //  * accumulation is fp32 in the matrix cores.  For wide models the fp32
 //    partial sums are carried into fp64 registers after every K step of 32, so
 //    the rounding error does not grow with K;
@@ -33,17 +35,25 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_CLS = 3 };
 constexpr int BK = 32;
 constexpr int LDS_STRIDE = BK + 4;
 
-// Global -> register loads of one K step: BM x 32 floats of A, BN x 32 of W
-// (8 float4 per row); rows past M / N read as zero.
-template <int ROWS, int NTHR, int L>
-__device__ __forceinline__ void tile_gload(float4 (&r)[L], const float* __restrict__ src, int row0,
+// Four consecutive elements idx .. idx+3 (idx a multiple of 4) of a weight
+// matrix held in fp32, or in bfloat16 (an 8-byte load, widened exactly).
+template <bool BF>
+__device__ __forceinline__ float4 load_w4(const void* W, size_t idx) {
+  if (BF) return bf16x4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) + idx));
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
+}
+
+// Global -> register loads of one K step: BM x 32 values of A, BN x 32 of W
+// (8 float4 per row); rows past M / N read as zero.  BF: the source is bfloat16.
+template <int ROWS, int NTHR, bool BF, int L>
+__device__ __forceinline__ void tile_gload(float4 (&r)[L], const void* __restrict__ src, int row0,
                                            int nrows, int K, int k0, int tid) {
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const int idx = tid + i * NTHR;
     const int row = idx >> 3, c4 = idx & 7, g = row0 + row;
     if (idx < ROWS * 8 && g < nrows)
-      r[i] = *reinterpret_cast<const float4*>(src + (size_t)g * K + k0 + c4 * 4);
+      r[i] = load_w4<BF>(src, (size_t)g * K + k0 + c4 * 4);
     else
       r[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -58,7 +68,7 @@ __device__ __forceinline__ void tile_sstore(const float4 (&r)[L], float* dst, in
   }
 }
 
-template <int WM, int WN, int MT, int NT, int EPI, bool CARRY>
+template <int WM, int WN, int MT, int NT, int EPI, bool CARRY, bool BF>
 __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int BM = 32 * MT * WM, BN = 32 * NT * WN;
@@ -87,8 +97,8 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
       for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[mt][nt][j] = 0.0;
     }
 
-  tile_gload<BM, NTHR>(ra, a.A, m0, M, K, 0, tid);
-  tile_gload<BN, NTHR>(rb, a.W, n0, N, K, 0, tid);
+  tile_gload<BM, NTHR, false>(ra, a.A, m0, M, K, 0, tid);
+  tile_gload<BN, NTHR, BF>(rb, a.W, n0, N, K, 0, tid);
   tile_sstore<BM, NTHR>(ra, As[0], tid);
   tile_sstore<BN, NTHR>(rb, Bs[0], tid);
   __syncthreads();
@@ -98,8 +108,8 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   for (int k0 = 0; k0 < K; k0 += BK) {
     const bool more = k0 + BK < K;
     if (more) {
-      tile_gload<BM, NTHR>(ra, a.A, m0, M, K, k0 + BK, tid);
-      tile_gload<BN, NTHR>(rb, a.W, n0, N, K, k0 + BK, tid);
+      tile_gload<BM, NTHR, false>(ra, a.A, m0, M, K, k0 + BK, tid);
+      tile_gload<BN, NTHR, BF>(rb, a.W, n0, N, K, k0 + BK, tid);
     }
     const float* as = As[cur];
     const float* bs = Bs[cur];
@@ -272,7 +282,7 @@ size_t sk_lds_bytes(int kc, bool carry) {
   return stage > red ? stage : red;
 }
 
-template <int EPI, bool CARRY>
+template <int EPI, bool CARRY, bool BF>
 __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int kz) {
   typedef typename SkAcc<CARRY>::T PT;
   extern __shared__ char sk_smem[];
@@ -336,13 +346,11 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (f < SK_ROWS * f4) {
         const int r = f / f4, c = f - r * f4;
-        const float* src = nullptr;
         if (r < 32) {
-          if (m0 + r < M) src = a.A + (size_t)(m0 + r) * K;
+          if (m0 + r < M) v = *reinterpret_cast<const float4*>(a.A + (size_t)(m0 + r) * K + kb + 4 * c);
         } else if (n0 + r - 32 < N) {
-          src = a.W + (size_t)(n0 + r - 32) * K;
+          v = load_w4<BF>(a.W, (size_t)(n0 + r - 32) * K + kb + 4 * c);
         }
-        if (src) v = *reinterpret_cast<const float4*>(src + kb + 4 * c);
       }
       st[i] = v;
     }
@@ -507,6 +515,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
 
 template <int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
+  if (a.K % BK != 0) return hipErrorInvalidValue;   // whole K steps (and 8-byte bfloat16 loads)
   const int nb = (a.N + 127) / 128;
   auto blocks = [&](int bm) { return ((a.M + bm - 1) / bm) * nb; };
   if (a.M <= 256 && blocks(a.M > 32 ? 64 : 32) < 256) {
@@ -530,20 +539,28 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     static bool lds_raised = false;
     if (!lds_raised) {
       const int most = (int)std::max(sk_lds_bytes(SK_KC, false), sk_lds_bytes(SK_KC, true));
-      hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_sk<EPI, false>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, most);
-      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_sk<EPI, true>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, most);
-      if (e1 != hipSuccess || e2 != hipSuccess) return e1 != hipSuccess ? e1 : e2;
+      const void* fns[4] = {reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, false>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, false>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, true>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, true>)};
+      for (const void* fn : fns) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        if (e != hipSuccess) return e;
+      }
       lds_raised = true;
     }
     if (nparts) *nparts = grid.x;
-    if (a.carry)
-      hipExtLaunchKernelGGL((k_gemm_sk<EPI, true>), grid, dim3(SK_THREADS), shmem, s, a.ev_start,
-                            a.ev_stop, 0, a, kc, kz);
-    else
-      hipExtLaunchKernelGGL((k_gemm_sk<EPI, false>), grid, dim3(SK_THREADS), shmem, s, a.ev_start,
-                            a.ev_stop, 0, a, kc, kz);
+#define LD_GEMM_SK_LAUNCH(CARRY, BF) \
+  hipExtLaunchKernelGGL((k_gemm_sk<EPI, CARRY, BF>), grid, dim3(SK_THREADS), shmem, s, a.ev_start, \
+                        a.ev_stop, 0, a, kc, kz)
+    if (a.bf16) {
+      if (a.carry) LD_GEMM_SK_LAUNCH(true, true);
+      else LD_GEMM_SK_LAUNCH(false, true);
+    } else {
+      if (a.carry) LD_GEMM_SK_LAUNCH(true, false);
+      else LD_GEMM_SK_LAUNCH(false, false);
+    }
+#undef LD_GEMM_SK_LAUNCH
     return hipGetLastError();
   }
   int bm;
@@ -555,13 +572,17 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     bm = 32;
   dim3 grid(nb, (a.M + bm - 1) / bm);
   if (nparts) *nparts = nb * 2;
-#define LD_GEMM_LAUNCH(WM, MT, THR)                                                             \
-  if (a.carry)                                                                                  \
-    hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, true>), grid, dim3(THR), 0, s, a.ev_start, \
-                          a.ev_stop, 0, a);                                                     \
-  else                                                                                          \
-    hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, false>), grid, dim3(THR), 0, s, a.ev_start, \
-                          a.ev_stop, 0, a);
+#define LD_GEMM_LAUNCH1(WM, MT, THR, CARRY, BF)                                                  \
+  hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, CARRY, BF>), grid, dim3(THR), 0, s, a.ev_start, \
+                        a.ev_stop, 0, a)
+#define LD_GEMM_LAUNCH(WM, MT, THR)                                      \
+  if (a.bf16) {                                                          \
+    if (a.carry) LD_GEMM_LAUNCH1(WM, MT, THR, true, true);               \
+    else LD_GEMM_LAUNCH1(WM, MT, THR, false, true);                      \
+  } else {                                                               \
+    if (a.carry) LD_GEMM_LAUNCH1(WM, MT, THR, true, false);              \
+    else LD_GEMM_LAUNCH1(WM, MT, THR, false, false);                     \
+  }
   if (bm == 128) {
     LD_GEMM_LAUNCH(2, 2, 256)
   } else if (bm == 64) {
@@ -570,6 +591,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     LD_GEMM_LAUNCH(1, 1, 128)
   }
 #undef LD_GEMM_LAUNCH
+#undef LD_GEMM_LAUNCH1
   return hipGetLastError();
 }
 

@@ -1,12 +1,14 @@
 // k_gemv.hip -- batch-1 projections of the decode step: y = W x for one token.
 //
-// At batch 1 every projection streams its whole fp32 weight matrix once per
-// token and does 2 flops per 4 bytes, so the bound is HBM bandwidth.  Design:
+// At batch 1 every projection streams its whole weight matrix once per token
+// and does 2 flops per 4 bytes (fp32) or per 2 bytes (bfloat16 weights, widened
+// exactly to fp32 in registers), so the bound is HBM bandwidth.  Design:
 //  * the input vector (RMS-normalised in the prologue where the step calls for
 //    it: the Q/K/V, W1/W3 and classifier projections) is staged once per
 //    workgroup in LDS as fp32, exactly as the pages' engine stores it;
 //  * each wave owns RW rows at a time; its 64 lanes stride across K with 16-byte
-//    loads, so one wave load instruction covers 1 KiB of a row and RW*U loads
+//    loads (4 fp32 or 8 bfloat16 weights), so one wave load instruction covers
+//    1 KiB of a row and RW*U loads
 //    are in flight per lane; the grid strides over row groups;
 //  * when the weights do not fit the 256 MB Infinity Cache the loads are
 //    non-temporal (streamed past the caches): on MI355X this lifts a pure read
@@ -36,6 +38,12 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_CLS = 3 };
 
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+// One 16-byte weight load: 4 fp32 weights, or 8 bfloat16 weights.
+template <bool BF> struct WVec;
+template <> struct WVec<false> { typedef float4 T; static constexpr int E = 4; };
+template <> struct WVec<true> { typedef uint4 T; static constexpr int E = 8; };
 
 template <bool NT>
 __device__ __forceinline__ float4 ld_w(const float4* p) {
@@ -44,6 +52,46 @@ __device__ __forceinline__ float4 ld_w(const float4* p) {
     return make_float4(t.x, t.y, t.z, t.w);
   }
   return *p;
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld_w(const uint4* p) {
+  if (NT) {
+    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+  }
+  return *p;
+}
+
+// x values of weight vector j (fp32: 4 of them, bfloat16: 8), held in double
+struct XVec4 { double v[4]; };
+struct XVec8f { float v[8]; };
+__device__ __forceinline__ XVec4 ld_x(const float4* xs4, int j, float4) {
+  const float4 a = xs4[j];
+  return XVec4{{a.x, a.y, a.z, a.w}};
+}
+__device__ __forceinline__ XVec8f ld_x(const float4* xs4, int j, uint4) {
+  const float4 a = xs4[2 * j], b = xs4[2 * j + 1];
+  return XVec8f{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+}
+__device__ __forceinline__ double dotw(const float4 w, const XVec4& x, double acc) {
+  return dot4(w, x.v[0], x.v[1], x.v[2], x.v[3], acc);
+}
+// bfloat16 weights: the 8 products of one 16-byte vector are summed in an fp32
+// chain, then carried into the fp64 accumulator.  (A bfloat16 x fp32 product has
+// up to 32 significant bits, so it is not exact in fp32: the chain's error is at
+// most ~8 units in the last place of its magnitude, ~5e-7 relative, two orders
+// below the logits' tolerance; converting every weight to fp64 instead measured
+// 3-35% slower per projection.)
+__device__ __forceinline__ double dotw(const uint4 w, const XVec8f& x, double acc) {
+  float c = bf16_lo(w.x) * x.v[0];
+  c = fmaf(bf16_hi(w.x), x.v[1], c);
+  c = fmaf(bf16_lo(w.y), x.v[2], c);
+  c = fmaf(bf16_hi(w.y), x.v[3], c);
+  c = fmaf(bf16_lo(w.z), x.v[4], c);
+  c = fmaf(bf16_hi(w.z), x.v[5], c);
+  c = fmaf(bf16_lo(w.w), x.v[6], c);
+  c = fmaf(bf16_hi(w.w), x.v[7], c);
+  return acc + (double)c;
 }
 
 // Stage x[0..K) into LDS; with a gain, replace it by RMSNorm(x) * gain rounded to fp32.
@@ -85,53 +133,73 @@ __device__ void stage_input(float* xs, const float* __restrict__ x, const float*
   __syncthreads();
 }
 
-template <int NR, int U, bool NT>
-__device__ __forceinline__ void load_batch(float4 (&w)[U][NR], const float4* (&rows)[NR], int it,
-                                           int lane) {
+template <int NR, int U, bool NT, typename T>
+__device__ __forceinline__ void load_batch(T (&w)[U][NR], const T* (&rows)[NR], int it, int lane) {
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[u][r] = ld_w<NT>(rows[r] + (it + u) * kWave + lane);
 }
 
-template <int NR, int U>
-__device__ __forceinline__ void fma_batch(const float4 (&w)[U][NR], const float4* xs4, int it, int lane,
+template <int NR, int U, typename T>
+__device__ __forceinline__ void fma_batch(const T (&w)[U][NR], const float4* xs4, int it, int lane,
                                           double (&acc)[NR]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const float4 xv = xs4[(it + u) * kWave + lane];
-    const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+    const auto xv = ld_x(xs4, (it + u) * kWave + lane, T{});
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = dot4(w[u][r], x0, x1, x2, x3, acc[r]);
+    for (int r = 0; r < NR; ++r) acc[r] = dotw(w[u][r], xv, acc[r]);
   }
 }
 
 // acc[r] += sum over this lane's slice of K of W_r . x  for NR row pointers,
-// starting at float4 column block `it` (the blocks before it are done already).
-template <int NR, int U, bool NT>
-__device__ __forceinline__ void dot_rows(const float4* (&rows)[NR], const float4* xs4, int K4,
-                                         int lane, double (&acc)[NR], int it) {
-  const int nfull = K4 >> 6;
+// starting at weight vector block `it` (the blocks before it are done already);
+// KV = weight vectors (16 bytes each) per row.
+// REM: what is left after the full batches (fewer than U whole blocks plus the
+// ragged tail, at most U blocks) is loaded as one predicated batch instead of
+// block by block.
+template <int NR, int U, bool NT, bool REM, typename T>
+__device__ __forceinline__ void dot_rows(const T* (&rows)[NR], const float4* xs4, int KV, int lane,
+                                         double (&acc)[NR], int it) {
+  const int nfull = KV >> 6;
   for (; it + U <= nfull; it += U) {
-    float4 w[U][NR];
+    T w[U][NR];
     load_batch<NR, U, NT>(w, rows, it, lane);
     fma_batch<NR, U>(w, xs4, it, lane, acc);
   }
+  if constexpr (REM) {
+    T w[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = (it + u) * kWave + lane;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        if (j < KV) w[u][r] = ld_w<NT>(rows[r] + j);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = (it + u) * kWave + lane;
+      if (j < KV) {
+        const auto xv = ld_x(xs4, j, T{});
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = dotw(w[u][r], xv, acc[r]);
+      }
+    }
+    return;
+  }
   for (; it < nfull; ++it) {
-    float4 w[NR];
+    T w[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = ld_w<NT>(rows[r] + it * kWave + lane);
-    const float4 xv = xs4[it * kWave + lane];
-    const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+    const auto xv = ld_x(xs4, it * kWave + lane, T{});
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = dot4(w[r], x0, x1, x2, x3, acc[r]);
+    for (int r = 0; r < NR; ++r) acc[r] = dotw(w[r], xv, acc[r]);
   }
   const int j = nfull * kWave + lane;
-  if (j < K4) {
-    const float4 xv = xs4[j];
-    const double x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+  if (j < KV) {
+    const auto xv = ld_x(xs4, j, T{});
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = dot4(ld_w<NT>(rows[r] + j), x0, x1, x2, x3, acc[r]);
+    for (int r = 0; r < NR; ++r) acc[r] = dotw(ld_w<NT>(rows[r] + j), xv, acc[r]);
   }
 }
 
@@ -145,14 +213,26 @@ __device__ __forceinline__ double pick(const double (&acc)[N], int i) {
   return v;
 }
 
-template <int EPI, int RW, int U, bool NT>
+// How a wave walks its row groups (grid-strided):
+//  MODE_PLAIN  load / use batch by batch, group by group;
+//  MODE_PIPE   the next group's first batch is issued before the current group's
+//              reduction and epilogue, so the memory pipe stays busy across groups;
+//  MODE_DB     rows of exactly one batch (64 * U vectors): two batch buffers,
+//              group g+1's loads are issued before group g's products, so two
+//              groups are in flight per wave.
+enum Mode { MODE_PLAIN = 0, MODE_PIPE = 1, MODE_DB = 2 };
+
+template <int EPI, int RW, int U, bool NT, bool BF, int MODE>
 __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
+  typedef typename WVec<BF>::T T;
+  constexpr int EB = BF ? 2 : 4;   // bytes per weight
   extern __shared__ float xs[];
   __shared__ double red[kWavesPerBlock];
   __shared__ float best_v[kWavesPerBlock];
   __shared__ int best_i[kWavesPerBlock];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K = a.K, K4 = K >> 2, N = a.N;
+  const int K = a.K, KV = K / WVec<BF>::E, N = a.N;
+  const char* wbase = static_cast<const char*>(a.W);
 
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * RW : RW;
   const int ngroups = (N + RW - 1) / RW;
@@ -161,16 +241,16 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   int bi = 0x7fffffff;
   bool nonfinite = false;
 
-  auto set_rows = [&](const float4* (&rows)[NR], int r0) {
+  auto set_rows = [&](const T* (&rows)[NR], int r0) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const int r = min(r0 + i, N - 1);   // rows past N are computed and dropped
       if (EPI == EPI_SWIGLU) {
         const size_t dev1 = (size_t)(r >> 5) * 64 + (r & 31);   // W1 row r
-        rows[i] = reinterpret_cast<const float4*>(a.W + dev1 * K);
-        rows[RW + i] = reinterpret_cast<const float4*>(a.W + (dev1 + 32) * K);   // W3 row r
+        rows[i] = reinterpret_cast<const T*>(wbase + dev1 * K * EB);
+        rows[RW + i] = reinterpret_cast<const T*>(wbase + (dev1 + 32) * K * EB);   // W3 row r
       } else {
-        rows[i] = reinterpret_cast<const float4*>(a.W + (size_t)r * K);
+        rows[i] = reinterpret_cast<const T*>(wbase + (size_t)r * K * EB);
       }
     }
   };
@@ -179,10 +259,10 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   // this wave's loads before staging (and normalising) x, so the prologue
   // overlaps the first HBM round trip.
   int grp = blockIdx.x * kWavesPerBlock + wave;
-  const float4* rows[NR];
+  const T* rows[NR];
   set_rows(rows, grp * RW);
-  float4 wpre[U][NR];
-  const bool pre = grp < ngroups && (K4 >> 6) >= U;
+  T wpre[U][NR];
+  bool pre = grp < ngroups && (KV >> 6) >= U;
   if (pre) load_batch<NR, U, NT>(wpre, rows, 0, lane);
 
   // position of the token (rotary angle, KV-cache slot); first needed by the
@@ -191,33 +271,29 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   stage_input(xs, a.x, a.gain, K, a.eps, red);
   const float4* xs4 = reinterpret_cast<const float4*>(xs);
 
-  for (bool first = true; grp < ngroups; grp += wstride, first = false) {
-    const int r0 = grp * RW;
-    if (!first) set_rows(rows, r0);
-    // lane i finishes row r0 + i: fetch what its epilogue reads now
+  // Lane i finishes row r0 + i.  What its epilogue reads (the residual element,
+  // the rotary cos / sin of its pair) is fetched before the group's products.
+  struct EpiIn {
+    float resid, rc, rs;
+  };
+  auto fetch_epi = [&](int r0) {
+    EpiIn e{0.f, 1.f, 0.f};
     const int my_r = r0 + lane;
     const bool mine = lane < RW && my_r < N;
-    float resid_in = 0.f;
-    if (EPI == EPI_RESID && mine) resid_in = a.resid[my_r];
-    float rc_in = 1.f, rs_in = 0.f;   // rotation of the pair (my_r, my_r + 1) for q and k rows
+    if (EPI == EPI_RESID && mine) e.resid = a.resid[my_r];
     if (EPI == EPI_QKV && mine && !(lane & 1) && my_r < a.d + a.kvh * a.hd) {
       const int ii = (my_r % a.d) % a.hd, t = pos * (a.hd >> 1) + (ii >> 1);
-      rc_in = a.rcos[t];
-      rs_in = a.rsin[t];
+      e.rc = a.rcos[t];
+      e.rs = a.rsin[t];
     }
-
-    double acc[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = 0.0;
-    int it0 = 0;
-    if (first && pre) {
-      fma_batch<NR, U>(wpre, xs4, 0, lane, acc);
-      it0 = U;
-    }
-    dot_rows<NR, U, NT>(rows, xs4, K4, lane, acc, it0);
+    return e;
+  };
+  // the wave's dot products are complete in acc: reduce and run the epilogue
+  auto finish = [&](int r0, double (&acc)[NR], const EpiIn& e) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
-
+    const int my_r = r0 + lane;
+    const bool mine = lane < RW && my_r < N;
     if (EPI == EPI_CLS) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
@@ -229,17 +305,17 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         }
       }
       if (a.logits != nullptr && mine) a.logits[my_r] = (float)pick(acc, lane);
-      continue;
+      return;
     }
-    if (!mine) continue;
+    if (!mine) return;
     if (EPI == EPI_QKV) {
       // lane i (even) rotates the pair (r0+i, r0+i+1); odd lanes hold the partner
-      if (lane & 1) continue;
+      if (lane & 1) return;
       float y0 = (float)pick(acc, lane), y1 = (float)pick(acc, lane + 1);
       const int d = a.d, hd = a.hd;
       int c;
       const int sec = qkv_section(my_r, d, a.kvh * hd, &c), h = c / hd, ii = c - h * hd;
-      if (sec < 2) rope_pair(y0, y1, rc_in, rs_in, y0, y1);
+      if (sec < 2) rope_pair(y0, y1, e.rc, e.rs, y0, y1);
       if (sec == 0) {
         a.q_out[c] = y0;
         a.q_out[c + 1] = y1;
@@ -253,7 +329,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         vrow[ii + 1] = y1;
       }
     } else if (EPI == EPI_RESID) {
-      a.resid[my_r] = resid_in + (float)pick(acc, lane);
+      a.resid[my_r] = e.resid + (float)pick(acc, lane);
     } else if (EPI == EPI_SWIGLU) {
       double h1 = 0.0, h3 = 0.0;
 #pragma unroll
@@ -263,6 +339,56 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
           h3 = acc[RW + k];
         }
       a.g_out[my_r] = swiglu((float)h1, (float)h3);
+    }
+  };
+
+  if constexpr (MODE == MODE_DB) {
+    // every row is one batch: buffers wpre (group g) and wnx (group g + wstride)
+    T wnx[U][NR];
+    auto group = [&](int g, const T (&w)[U][NR], const EpiIn& e) {
+      double acc[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = 0.0;
+      fma_batch<NR, U>(w, xs4, 0, lane, acc);
+      finish(g * RW, acc, e);
+    };
+    for (; grp < ngroups; grp += 2 * wstride) {
+      const int g1 = grp + wstride, g2 = g1 + wstride;
+      const EpiIn e0 = fetch_epi(grp * RW);   // before the next loads: waited for without them
+      if (g1 < ngroups) {
+        set_rows(rows, g1 * RW);
+        load_batch<NR, U, NT>(wnx, rows, 0, lane);
+      }
+      group(grp, wpre, e0);
+      if (g1 >= ngroups) break;
+      const EpiIn e1 = fetch_epi(g1 * RW);
+      if (g2 < ngroups) {
+        set_rows(rows, g2 * RW);
+        load_batch<NR, U, NT>(wpre, rows, 0, lane);
+      }
+      group(g1, wnx, e1);
+    }
+  } else {
+    for (bool first = true; grp < ngroups; grp += wstride, first = false) {
+      const int r0 = grp * RW;
+      if (!first && MODE != MODE_PIPE) set_rows(rows, r0);
+      const EpiIn e = fetch_epi(r0);
+      double acc[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = 0.0;
+      int it0 = 0;
+      if ((first || MODE == MODE_PIPE) && pre) {
+        fma_batch<NR, U>(wpre, xs4, 0, lane, acc);
+        it0 = U;
+      }
+      dot_rows<NR, U, NT, MODE == MODE_PIPE>(rows, xs4, KV, lane, acc, it0);
+      if (MODE == MODE_PIPE) {
+        const int ng = grp + wstride;
+        if (ng < ngroups) set_rows(rows, ng * RW);
+        pre = ng < ngroups && (KV >> 6) >= U;
+        if (pre) load_batch<NR, U, NT>(wpre, rows, 0, lane);
+      }
+      finish(r0, acc, e);
     }
   }
 
@@ -283,7 +409,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   }
 }
 
-template <int EPI, int RW, int U, bool NT>
+template <int EPI, int RW, int U, bool NT, bool BF, int MODE>
 hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blocks_out) {
   const int groups = (a.N + RW - 1) / RW;
   int blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -291,10 +417,10 @@ hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blo
   if (blocks_out) *blocks_out = blocks;
   const size_t shmem = (size_t)a.K * sizeof(float);
   if (a.ev_start != nullptr)
-    hipExtLaunchKernelGGL((k_gemv<EPI, RW, U, NT>), dim3(blocks), dim3(kThreads), shmem, s, a.ev_start,
+    hipExtLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE>), dim3(blocks), dim3(kThreads), shmem, s, a.ev_start,
                           a.ev_stop, 0, a);
   else
-    hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT>), dim3(blocks), dim3(kThreads), shmem, s, a);
+    hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE>), dim3(blocks), dim3(kThreads), shmem, s, a);
   return hipGetLastError();
 }
 
@@ -302,12 +428,26 @@ hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blo
 // in the Infinity Cache from one token to the next.
 bool streamed(const GemvArgs& a) { return a.stream; }
 
-template <int EPI, int RW, int U>
+template <int EPI, int RW, int U, bool BF>
 hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
   constexpr int kMaxBlocks = 512;   // 2 resident workgroups per CU on 256 CUs; the grid strides beyond
-  if (streamed(a)) return launch_cfg<EPI, RW, U, true>(a, kMaxBlocks, s, blocks_out);
-  return launch_cfg<EPI, RW, U, false>(a, kMaxBlocks, s, blocks_out);
+  if (a.bf16 != BF || a.K % WVec<true>::E != 0) return hipErrorInvalidValue;   // whole 16-byte vectors
+  if constexpr (!BF) {   // fp32 rows hold several batches; the plain walk measured best
+    if (streamed(a)) return launch_cfg<EPI, RW, U, true, BF, MODE_PLAIN>(a, kMaxBlocks, s, blocks_out);
+    return launch_cfg<EPI, RW, U, false, BF, MODE_PLAIN>(a, kMaxBlocks, s, blocks_out);
+  } else {
+    // bfloat16 rows are half as many bytes: keep loads in flight across row groups
+    if (a.K / WVec<BF>::E == kWave * U) {
+      if (streamed(a)) return launch_cfg<EPI, RW, U, true, BF, MODE_DB>(a, kMaxBlocks, s, blocks_out);
+      return launch_cfg<EPI, RW, U, false, BF, MODE_DB>(a, kMaxBlocks, s, blocks_out);
+    }
+    if (streamed(a)) return launch_cfg<EPI, RW, U, true, BF, MODE_PIPE>(a, kMaxBlocks, s, blocks_out);
+    return launch_cfg<EPI, RW, U, false, BF, MODE_PIPE>(a, kMaxBlocks, s, blocks_out);
+  }
 }
+
+// Rows per wave for bfloat16 weights (a row is half as many bytes as in fp32).
+constexpr int kBfRwQkv = 2, kBfRwResid = 2, kBfRwResidLong = 1, kBfRwSwiglu = 1, kBfRwCls = 2;
 
 }  // namespace
 
@@ -315,18 +455,25 @@ hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
 // of U 16-byte loads per row in flight).
 hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s) {
   if (a.kvh <= 0 || a.N != a.d + 2 * a.kvh * a.hd) return hipErrorInvalidValue;
-  return launch<EPI_QKV, 2, 8>(a, s);
+  if (a.bf16) return launch<EPI_QKV, kBfRwQkv, 8, true>(a, s);
+  return launch<EPI_QKV, 2, 8, false>(a, s);
 }
 hipError_t launch_gemv_resid(const GemvArgs& a, hipStream_t s) {
   // long rows (W2: K = hidden width) keep more rows in flight with one row per wave
-  if (a.K >= 8192) return launch<EPI_RESID, 1, 8>(a, s);
-  return launch<EPI_RESID, 2, 8>(a, s);
+  if (a.bf16) {
+    if (a.K >= 8192) return launch<EPI_RESID, kBfRwResidLong, 8, true>(a, s);
+    return launch<EPI_RESID, kBfRwResid, 8, true>(a, s);
+  }
+  if (a.K >= 8192) return launch<EPI_RESID, 1, 8, false>(a, s);
+  return launch<EPI_RESID, 2, 8, false>(a, s);
 }
 hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s) {
-  return launch<EPI_SWIGLU, 1, 8>(a, s);
+  if (a.bf16) return launch<EPI_SWIGLU, kBfRwSwiglu, 8, true>(a, s);
+  return launch<EPI_SWIGLU, 1, 8, false>(a, s);
 }
 hipError_t launch_gemv_cls(const GemvArgs& a, int* nparts, hipStream_t s) {
-  return launch<EPI_CLS, 2, 8>(a, s, nparts);
+  if (a.bf16) return launch<EPI_CLS, kBfRwCls, 8, true>(a, s, nparts);
+  return launch<EPI_CLS, 2, 8, false>(a, s, nparts);
 }
 
 }  // namespace ld

@@ -7,9 +7,10 @@ namespace ld {
 
 namespace {
 
-// x[r] = E[tok[r]]; an out-of-range id (only possible for ids read from device
-// memory) is replaced by 0 and flagged.
-__global__ void __launch_bounds__(256) k_embed(const int* tok, const float* E, float* x, int d, int V,
+// x[r] = E[tok[r]] (a bfloat16 table widened exactly when BF); an out-of-range
+// id (only possible for ids read from device memory) is replaced by 0 and flagged.
+template <bool BF>
+__global__ void __launch_bounds__(256) k_embed(const int* tok, const void* E, float* x, int d, int V,
                                                int* err, const int* pos_src, int* pos_dst) {
   const int r = blockIdx.x;
   if (pos_dst != nullptr && r == 0 && threadIdx.x == 0) *pos_dst = *pos_src;
@@ -18,9 +19,14 @@ __global__ void __launch_bounds__(256) k_embed(const int* tok, const float* E, f
     if (threadIdx.x == 0) atomicOr(err, 2);
     t = 0;
   }
-  const float4* src = reinterpret_cast<const float4*>(E + (size_t)t * d);
   float4* dst = reinterpret_cast<float4*>(x + (size_t)r * d);
-  for (int j = threadIdx.x; j < (d >> 2); j += 256) dst[j] = src[j];
+  if (BF) {
+    const uint2* src = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(E) + (size_t)t * d);
+    for (int j = threadIdx.x; j < (d >> 2); j += 256) dst[j] = bf16x4(src[j]);
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(E) + (size_t)t * d);
+    for (int j = threadIdx.x; j < (d >> 2); j += 256) dst[j] = src[j];
+  }
 }
 
 // out[i] = RMSNorm(in[i * in_stride + in_offset]) * gain, rounded to fp32.
@@ -99,9 +105,12 @@ __global__ void k_set_int(int* p, int v) {
 
 }  // namespace
 
-hipError_t launch_embed(const int* tok, const float* E, float* x, int rows, int d, int V, int* err,
-                        const int* pos_src, int* pos_dst, hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst);
+hipError_t launch_embed(const int* tok, const void* E, bool bf16, float* x, int rows, int d, int V,
+                        int* err, const int* pos_src, int* pos_dst, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(k_embed<true>, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst);
+  else
+    hipLaunchKernelGGL(k_embed<false>, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst);
   return hipGetLastError();
 }
 

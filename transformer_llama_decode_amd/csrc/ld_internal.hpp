@@ -56,7 +56,8 @@ struct GemvArgs {
   const float* x;      // input vector [K]
   const float* gain;   // RMSNorm gain [K], or nullptr: no normalisation
   double eps;
-  const float* W;      // rows of K floats
+  const void* W;      // rows of K weights: fp32, or bfloat16 when bf16
+  bool bf16;
   int N, K;
   bool stream;         // non-temporal weight loads (weights larger than the Infinity Cache)
   hipEvent_t ev_start, ev_stop;   // when set, recorded by the dispatch itself (timing)
@@ -105,7 +106,8 @@ hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s);
 
 struct GemmArgs {
   const float* A;      // [M][K]
-  const float* W;      // [N][K]
+  const void* W;      // [N][K], fp32, or bfloat16 when bf16 (widened exactly on load)
+  bool bf16;
   int M, N, K;
   bool carry;          // fp32 MFMA partial sums carried into fp64 every 32 k
   hipEvent_t ev_start, ev_stop;   // when set, recorded by the dispatch itself (timing)
@@ -145,8 +147,8 @@ hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_cls(const GemmArgs& a, int* nparts, hipStream_t s);
 
 // pos_dst/pos_src (both or neither): the first workgroup also copies *pos_src to *pos_dst
-hipError_t launch_embed(const int* tok, const float* E, float* x, int rows, int d, int V, int* err,
-                        const int* pos_src, int* pos_dst, hipStream_t s);
+hipError_t launch_embed(const int* tok, const void* E, bool bf16, float* x, int rows, int d, int V,
+                        int* err, const int* pos_src, int* pos_dst, hipStream_t s);
 // out row i <- rmsnorm(in row i * in_stride + in_offset)
 hipError_t launch_rmsnorm_rows(const float* in, float* out, const float* gain, int rows, int d,
                                int in_stride, int in_offset, double eps, hipStream_t s);

@@ -14,8 +14,8 @@ from .configs import ModelConfig
 
 def _cfg_struct(cfg: ModelConfig):
     return LdConfig(cfg.dim, cfg.n_layers, cfg.n_heads, cfg.hidden_dim, cfg.vocab_size, cfg.max_seq,
-                    cfg.max_batch, int(cfg.tied), int(cfg.n_kv_heads or 0), float(cfg.rope_theta),
-                    float(cfg.norm_eps))
+                    cfg.max_batch, int(cfg.tied), int(cfg.n_kv_heads or 0), int(bool(cfg.weight_bf16)),
+                    float(cfg.rope_theta), float(cfg.norm_eps))
 
 
 def arena_bytes(cfg: ModelConfig) -> int:

@@ -37,11 +37,13 @@ def log(*a):
 def step_bytes(cfg, pos, batch=1):
     """Algorithmic HBM bytes of one decode step at position pos: every matrix
     once, plus per sequence the embedding row, norm gains, the K/V history read
-    (positions 0..pos), the new K/V written and the logits written."""
+    (positions 0..pos, or the max_seq of them in the window past max_seq), the
+    new K/V written and the logits written."""
     d, f, V, L, kvd = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers, cfg.kv_dim
     weights = cfg.weight_elem_bytes * (L * (2 * d * d + 2 * kvd * d + 3 * d * f) + V * d)
     gains = 4 * (2 * L + 1) * d
-    per_seq = 4 * (d + 2 * L * (pos + 1) * kvd + 2 * L * kvd + V)
+    seen = min(pos + 1, cfg.max_seq)
+    per_seq = 4 * (d + 2 * L * seen * kvd + 2 * L * kvd + V)
     return weights + gains + batch * per_seq
 
 
@@ -211,8 +213,8 @@ def main():
     B = w.batch
     P = max(w.prompt_len, 1)
     steps = min(args.steps, w.end_pos - P)
-    if P + max(steps, args.warmup) > cfg.max_seq:
-        sys.exit("steps + prompt exceed max_seq %d" % cfg.max_seq)
+    if P + max(steps, args.warmup) > cfg.positions:
+        sys.exit("steps + prompt exceed the model's %d positions" % cfg.positions)
     dev = torch.device("cuda", 0)
     t0 = time.time()
     gm = LlamaDecoder(cfg, w.model_seed)
@@ -268,7 +270,12 @@ def main():
     # the stream for a few microseconds, so they stay out of the throughput pass).
     classes = [_lib.LD_K_W13] if B == 1 else [_lib.LD_K_QKV, _lib.LD_K_WO, _lib.LD_K_W13,
                                               _lib.LD_K_W2, _lib.LD_K_CLS]
-    gm.set_pos(P)
+    if gm.set_pos_rc(P) != 0:
+        # past max_seq the ring no longer holds position P's window: time the next
+        # positions instead (the step's work does not depend on the position there)
+        if gm.pos + steps > cfg.positions:
+            sys.exit("no positions left for the kernel timing pass")
+        log("kernel timing pass at positions %d..%d" % (gm.pos, gm.pos + steps - 1))
     for k in classes:
         gm.profile(k, True)
     run(steps, start_tok)

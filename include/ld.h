@@ -13,8 +13,11 @@
  * no equations; each step follows its published definition (RMSNorm: Zhang &
  * Sennrich 2019 eq. 4; rotary embedding: Su et al. 2021 eq. 34 with adjacent
  * pairs; SwiGLU: Shazeer 2020 sec. 2; block layout: Touvron et al. 2023 sec. 2.2).
- * Decoding stops at max_seq positions, as the pages' TODO about running past
- * max_seq_len says (openai.wiki "llama2.c | Baby LLaMA", "Unsorted TODO").
+ * The pages' engine stops at max_seq_len positions and lists running past it,
+ * with the KV cache taken into account, as a TODO (openai.wiki "llama2.c | Baby
+ * LLaMA", "Unsorted TODO").  Here decoding stops at max_pos positions (default
+ * max_seq); past max_seq the cache keeps the max_seq most recent positions and
+ * attention covers exactly those (see max_pos).
  *
  * Conventions for every call:
  *  - Return LD_OK (0) or a negative LD_E_* code.  On error no state changes.
@@ -41,7 +44,7 @@ extern "C" {
 
 #define LD_OK 0
 #define LD_E_INVAL -1     /* bad argument: config, batch, token id, NULL pointer */
-#define LD_E_RANGE -2     /* position would pass max_seq */
+#define LD_E_RANGE -2     /* position would pass max_pos, or a rewind past the cache */
 #define LD_E_ARENA -3     /* arena too small or misaligned */
 #define LD_E_HIP -4       /* a HIP runtime call failed */
 #define LD_E_NONFINITE -5 /* a logit was NaN or infinite, or a device token was out of range */
@@ -53,7 +56,7 @@ typedef struct {
   int32_t n_heads;         /* H; head_dim = dim / n_heads, a multiple of 16, <= 256 */
   int32_t hidden_dim;      /* SwiGLU width f; multiple of 32 */
   int32_t vocab_size;      /* V */
-  int32_t max_seq;         /* positions held by the KV cache */
+  int32_t max_seq;         /* positions held by the KV cache (the attention window) */
   int32_t max_batch;       /* sequences decoded in lockstep, >= 1 */
   int32_t tied_classifier; /* 1: classifier = token embedding; 0: separate matrix */
   int32_t n_kv_heads;      /* key/value heads, dividing n_heads; 0 = n_heads.  Fewer than
@@ -73,6 +76,15 @@ typedef struct {
                               engine is fp32 only (openai.wiki "llama2.c | Baby LLaMA",
                               intro; Xinzhiyuan's llama2.c report, intro); this halves the
                               bytes a decode step streams. */
+  int32_t max_pos;         /* positions the model may run through; 0 = max_seq, else >= max_seq.
+                              Past max_seq, position p attends to positions
+                              p - max_seq + 1 .. p (a sliding window: Beltagy et al. 2020,
+                              Longformer, sec. 3.1; Jiang et al. 2023, Mistral 7B, sec. 2),
+                              rotary angles of the absolute position; the KV cache is then a
+                              ring of max_seq rounded up to 64, plus 64, slots per sequence
+                              (position p in slot p mod ring) and long prompts are processed
+                              in chunks that never overwrite a slot a row of the chunk still
+                              sees.  Rotary tables hold max_pos positions. */
   double rope_theta;       /* rotary base, 10000 for Llama-2 */
   double norm_eps;         /* RMSNorm epsilon, added inside the square root */
 } ld_config;
@@ -98,7 +110,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
  * last position's logits to dev_logits[batch][V] (or every position's to
  * dev_logits[batch][n_tokens][V] when all_pos != 0; NULL = not written) and
  * the greedy next token of each sequence to dev_next[batch] (NULL = not
- * written).  Then pos += n_tokens.  LD_E_RANGE if pos + n_tokens > max_seq. */
+ * written).  Then pos += n_tokens.  LD_E_RANGE if pos + n_tokens > max_pos. */
 int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host_tokens,
                float* dev_logits, int32_t* dev_next, int32_t all_pos);
 
@@ -107,7 +119,8 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
  * previous step's dev_next; an out-of-range device id is replaced by 0 and
  * reported by ld_status as LD_E_NONFINITE).  Writes logits [batch][V] to
  * dev_logits (NULL = not written) and the greedy tokens (lowest index among
- * equal maxima) to dev_next (NULL = not written).  Then pos += 1. */
+ * equal maxima) to dev_next (NULL = not written).  Then pos += 1.  LD_E_RANGE
+ * if pos + 1 > max_pos. */
 int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
                    float* dev_logits, int32_t* dev_next);
 
@@ -123,8 +136,8 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
  * (NULL = not written).  The step is captured once as a HIP graph per (batch,
  * dev_logits) and replayed; a different pair recaptures it.  Same results as
  * n calls of ld_decode_step fed with their own dev_next, up to the rounding
- * of the attention split (fixed here by max_seq rather than the position).
- * Then pos += n_steps.  LD_E_RANGE if pos + n_steps > max_seq; n_steps == 0
+ * of the attention split (fixed here by the cache size rather than the position).
+ * Then pos += n_steps.  LD_E_RANGE if pos + n_steps > max_pos; n_steps == 0
  * does nothing. */
 int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* tokens,
                 int32_t tokens_on_device, float* dev_logits, int32_t* dev_out);
@@ -133,7 +146,9 @@ int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* toke
 int ld_kv_reset(ld_model* m);
 
 /* Rewind: pos := new_pos, 0 <= new_pos <= current pos (positions >= new_pos
- * are recomputed by later calls). */
+ * are recomputed by later calls).  Past max_seq the cache must still hold
+ * new_pos's window: LD_E_RANGE if new_pos - max_seq < pos - ring (ring = the
+ * cache's slots per sequence) once pos > ring. */
 int ld_set_pos(ld_model* m, int32_t new_pos);
 
 int ld_get_pos(const ld_model* m, int32_t* pos);

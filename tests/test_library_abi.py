@@ -66,10 +66,10 @@ def _cfg(m, **kw):
                                  dict(max_seq=0), dict(max_batch=0), dict(rope_theta=0.0),
                                  dict(dim=64, n_heads=1, hidden_dim=64, vocab_size=10, max_seq=4) | {"n_layers": 0},
                                  dict(dim=512, n_heads=1), dict(n_kv_heads=3), dict(n_kv_heads=-1),
-                                 dict(weight_bf16=2)])
+                                 dict(weight_bf16=2), dict(max_pos=50), dict(max_pos=-1)])
 def test_arena_bytes_rejects_unsupported_configs(L, bad):
     n = C.c_size_t(0)
-    raw = {k: bad.pop(k) for k in list(bad) if k == "weight_bf16"}   # set on the C struct as is
+    raw = {k: bad.pop(k) for k in list(bad) if k in ("weight_bf16", "max_pos")}   # set on the C struct as is
     c = _cfg(TINY, **bad)
     for k, v in raw.items():
         setattr(c, k, v)
@@ -129,3 +129,20 @@ def test_bfloat16_arena_halves_the_matrices(L):
         assert L.ld_arena_bytes(C.byref(_cfg(replace(m, weight_bf16=True))), C.byref(n16)) == 0
         matrices = m.n_params() - (2 * m.n_layers + 1) * m.dim      # all but the norm gains
         assert abs((n32.value - n16.value) - 2 * matrices) <= 16 * 256, tied
+
+
+def test_window_arena_adds_the_ring_slack_and_rotary_rows(L):
+    """past max_seq: 64 more KV slots per sequence and rotary rows for every position"""
+    from dataclasses import replace
+    m = ModelConfig(dim=128, n_layers=2, n_heads=4, hidden_dim=160, vocab_size=301, max_seq=100,
+                    max_batch=3, n_kv_heads=2)
+    n0, n1 = C.c_size_t(0), C.c_size_t(0)
+    assert L.ld_arena_bytes(C.byref(_cfg(m)), C.byref(n0)) == 0
+    assert L.ld_arena_bytes(C.byref(_cfg(replace(m, max_pos=1000))), C.byref(n1)) == 0
+    kv_slack = 2 * 4 * m.n_layers * m.max_batch * m.kv_dim * 64        # K and V, 64 slots
+    rope = 2 * 4 * (1000 - 100) * (m.head_dim // 2)                  # cos and sin rows
+    ring = 3 * 4 * (1000 - 100)                                      # generated-token ring
+    assert abs((n1.value - n0.value) - (kv_slack + rope + ring)) <= 16 * 256
+    n2 = C.c_size_t(0)
+    assert L.ld_arena_bytes(C.byref(_cfg(replace(m, max_pos=100))), C.byref(n2)) == 0
+    assert n2.value == n0.value                                      # max_pos = max_seq: no window

@@ -31,7 +31,8 @@ class LdConfig(C.Structure):
     _fields_ = [("dim", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
                 ("hidden_dim", C.c_int32), ("vocab_size", C.c_int32), ("max_seq", C.c_int32),
                 ("max_batch", C.c_int32), ("tied_classifier", C.c_int32),
-                ("n_kv_heads", C.c_int32), ("weight_bf16", C.c_int32), ("rope_theta", C.c_double),
+                ("n_kv_heads", C.c_int32), ("weight_bf16", C.c_int32), ("max_pos", C.c_int32),
+                ("rope_theta", C.c_double),
                 ("norm_eps", C.c_double)]
 
 

@@ -109,6 +109,11 @@ WORKLOADS = {
     "C5bf16": Workload("C5bf16", replace(M7B, weight_bf16=True), 4, 1, 512, 4, 1024,
                        description="7B shape, bfloat16 weights, b1, 512-token prompt, "
                                    "512 decode steps"),
+    # the 7B shape decoding past its KV cache: a 512-position window (max_seq 512,
+    # max_pos 2048), a 1024-token prompt, then positions 1024..1535 over the ring
+    "C5w": Workload("C5w", replace(M7B, max_seq=512, max_pos=2048), 4, 1, 1024, 4, 1536,
+                    description="7B shape, 512-position sliding window past max_seq, b1, "
+                                "1024-token prompt, 512 decode steps"),
     # grouped-query variant of the 7B shape: 8 key/value heads shared by groups of 4
     # query heads (a measurement of the grouped-query row; not one of the five configs)
     "C5g8": Workload("C5g8", replace(M7B, n_kv_heads=8), 4, 1, 512, 4, 1024,

@@ -18,7 +18,8 @@
 //    sum).
 // A chunk's first tile is c whatever the position, so when the position sits in
 // device memory (graph replays) the first tile's loads are issued before it
-// arrives.
+// arrives.  Keys are cache slots; which position a slot holds and whether the
+// query sees it (causality, and the sliding window past max_seq) is KvRing's.
 #pragma once
 
 #include "dev_common.hpp"
@@ -117,7 +118,10 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   const bool q_lane = threadIdx.x < HD / 4;   // HD / 4 <= 64 < kThreads
   const float4 qv_in = q_lane ? q4[threadIdx.x] : make_float4(0.f, 0.f, 0.f, 0.f);
   const int pos = spec ? *a.pos_dev : a.pos;
-  const int kvlen = pos + t + 1;
+  const int q = pos + t;                                    // this row's position
+  const KvRing kr(a.seq_pad, a.window, pos + a.n_tok - 1);
+  const int lo_q = kr.lo(q);
+  const int kvlen = min(q + 1, kr.nslots);                  // slots to visit
   const int ntiles = (kvlen + kTile - 1) / kTile;
   if (!spec && c < ntiles) load_tile<HD>(cur, kt, vb, c, w, lane);   // first tile in flight
   if (q_lane) qs4[threadIdx.x] = qv_in;
@@ -144,10 +148,11 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
     sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     __syncthreads();
     // ---- online softmax (every wave derives the same m, l from the same scores)
-    const bool valid = j0 + lane < kvlen;
+    const bool valid = j0 + lane < kvlen && kr.visible(j0 + lane, q, lo_q);
     const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
     const double m_new = fmax(m_run, wave_max(valid ? sc : -INFINITY));
-    const double scale = exp(m_run - m_new);   // 0 on the first tile (m_run = -inf)
+    // 0 on the first tile with a visible key (m_run = -inf); 1 while none was visible
+    const double scale = m_new == -INFINITY ? 1.0 : exp(m_run - m_new);
     const double e = valid ? exp(sc - m_new) : 0.0;
     if (w == 0) es[lane] = e;
     l_run = l_run * scale + wave_sum(e);
@@ -211,7 +216,8 @@ __device__ __forceinline__ void attn_rows(const AttnArgs a, int h, int b, int t0
   const float* vb = a.vc + head_off;
   const double sqrt_hd = sqrt((double)HD);
   const int pos = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
-  const int kvlen_max = pos + t0 + nrows;   // history of the last row
+  const KvRing kr(a.seq_pad, a.window, pos + a.n_tok - 1);
+  const int kvlen_max = min(pos + t0 + nrows, kr.nslots);   // slots the last row visits
   const int ntiles = (kvlen_max + kTile - 1) / kTile;
 
   TileRegs<HD> cur;
@@ -238,7 +244,8 @@ __device__ __forceinline__ void attn_rows(const AttnArgs a, int h, int b, int t0
     mask_tile<HD>(cur, tile, kvlen_max, w);
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      const int kvlen = pos + t0 + rr + 1;
+      const int q = pos + t0 + rr, lo_q = kr.lo(q);
+      const int kvlen = min(q + 1, kr.nslots);
       if (rr >= nrows || j0 >= kvlen) continue;   // uniform: this tile is past row rr's history
       double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -251,10 +258,10 @@ __device__ __forceinline__ void attn_rows(const AttnArgs a, int h, int b, int t0
       }
       sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       __syncthreads();
-      const bool valid = j0 + lane < kvlen;
+      const bool valid = j0 + lane < kvlen && kr.visible(j0 + lane, q, lo_q);
       const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
       const double m_new = fmax(m_run[rr], wave_max(valid ? sc : -INFINITY));
-      const double scale = exp(m_run[rr] - m_new);
+      const double scale = m_new == -INFINITY ? 1.0 : exp(m_run[rr] - m_new);
       const double e = valid ? exp(sc - m_new) : 0.0;
       if (w == 0) es[lane] = e;
       l_run[rr] = l_run[rr] * scale + wave_sum(e);

@@ -111,4 +111,31 @@ __device__ __forceinline__ size_t ktile_index(int p, int i, int hd) {
   return (((size_t)(p >> 6) * (hd >> 2) + (i >> 2)) * 64 + (p & 63)) * 4 + (i & 3);
 }
 
+// The KV cache of a sequence has `ring` slots (a multiple of 64); position p is
+// stored in slot p mod ring.  Below `ring` positions that is slot p; a model
+// that runs past max_seq keeps rolling through the slots.
+__device__ __forceinline__ int kv_slot(int p, int ring) { return p < ring ? p : p % ring; }
+
+// Which position each slot holds after a pass whose last position is pmax, and
+// which of them a query sees: slot s holds the latest position congruent to s
+// (mod ring) that is <= pmax (negative: never written), and a query at position
+// q attends to positions max(0, q - window + 1) .. q (window = max_seq, the
+// sliding window past it; below max_seq simply the whole history).
+struct KvRing {
+  int ring, window, cut, lap, nslots;
+  __device__ __forceinline__ KvRing(int ring_, int window_, int pmax)
+      : ring(ring_), window(window_) {
+    cut = pmax < ring_ ? pmax : pmax % ring_;
+    lap = pmax - cut;                                // position held by slot 0 in this lap
+    nslots = pmax < ring_ ? pmax + 1 : ring_;       // slots written so far
+  }
+  __device__ __forceinline__ int pos_of(int s) const { return lap + s - (s > cut ? ring : 0); }
+  // lowest visible position of a query at q
+  __device__ __forceinline__ int lo(int q) const { return q - window + 1 > 0 ? q - window + 1 : 0; }
+  __device__ __forceinline__ bool visible(int s, int q, int lo_q) const {
+    const int p = pos_of(s);
+    return p >= lo_q && p <= q;
+  }
+};
+
 }  // namespace ld

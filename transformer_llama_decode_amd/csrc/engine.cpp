@@ -33,6 +33,17 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // key/value heads (grouped-query attention); 0 in the config means n_heads
 int kv_heads(const ld_config* c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
 
+// positions the model may run through (max_pos; 0 means max_seq)
+int positions(const ld_config* c) { return c->max_pos > 0 ? c->max_pos : c->max_seq; }
+
+// KV slots per sequence.  Past max_seq the cache is a ring: 64 slots beyond the
+// window let a prompt chunk of up to 65 positions write its keys without
+// overwriting any position an earlier row of the chunk still sees.
+size_t kv_ring(const ld_config* c) {
+  const size_t Sp = round_up((size_t)c->max_seq, 64);
+  return positions(c) > c->max_seq ? Sp + 64 : Sp;
+}
+
 int validate(const ld_config* c) {
   if (c == nullptr) return LD_E_INVAL;
   if (c->dim <= 0 || c->dim % 32 != 0 || c->dim > 16384) return LD_E_INVAL;
@@ -47,6 +58,8 @@ int validate(const ld_config* c) {
   if (c->max_batch <= 0 || c->max_batch > 4096) return LD_E_INVAL;
   if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0)) return LD_E_INVAL;
   if (c->weight_bf16 != 0 && c->weight_bf16 != 1) return LD_E_INVAL;
+  if (c->max_pos < 0 || c->max_pos > (1 << 24) || (c->max_pos > 0 && c->max_pos < c->max_seq))
+    return LD_E_INVAL;
   return LD_OK;
 }
 
@@ -54,7 +67,8 @@ void make_layout(const ld_config* c, Layout* L) {
   const size_t d = c->dim, f = c->hidden_dim, V = c->vocab_size, NL = c->n_layers,
                H = c->n_heads, hd = d / H, S = c->max_seq, B = c->max_batch;
   const size_t kvd = (size_t)kv_heads(c) * hd;   // rows of Wk and of Wv
-  const size_t Sp = round_up(S, 64);
+  const size_t Sp = kv_ring(c);                   // KV slots per sequence
+  const size_t P = (size_t)positions(c);
   const size_t es = c->weight_bf16 ? 2 : 4;       // bytes per matrix element
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -73,8 +87,8 @@ void make_layout(const ld_config* c, Layout* L) {
   L->layer0 = take(L->layer_stride * NL);
   L->Wcls = c->tied_classifier ? L->E : take(V * d * es);
   L->gain_final = take(d * 4);
-  L->rope_cos = take(S * (hd / 2) * 4);
-  L->rope_sin = take(S * (hd / 2) * 4);
+  L->rope_cos = take(P * (hd / 2) * 4);
+  L->rope_sin = take(P * (hd / 2) * 4);
   L->Kc = take(NL * B * kvd * Sp * 4);
   L->Vc = take(NL * B * kvd * Sp * 4);
   const size_t R = std::max(B, std::min((size_t)kMaxRowsCap, B * S));
@@ -96,7 +110,7 @@ void make_layout(const ld_config* c, Layout* L) {
   L->next = take(R * 4);
   L->err = take(4);
   L->pos_dev = take(2 * 4);
-  L->gen = take(S * B * 4);
+  L->gen = take(P * B * 4);
   L->total = off;
 }
 
@@ -371,6 +385,7 @@ int layers_gemv(ld_model* m, int pos) {
       a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev; a.kvh = m->kvh;
+      a.window = c.max_seq;
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
@@ -435,6 +450,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       a.ticket = m->at<int>(m->lay.attn_ticket);
       a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev; a.kvh = m->kvh;
+      a.window = c.max_seq;
       LD_TRY_HIP(launch_attention(a, m->stream));
     }
     {
@@ -679,8 +695,9 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
     if (launch_fill(m->at<float>(L.gain_final), 1.0f, d, m->stream) != hipSuccess) return fail(LD_E_HIP);
     // rotary tables: angle p * theta^(-2i/hd), cos/sin in double, stored fp32
     const int half = m->hd / 2;
-    std::vector<float> ct((size_t)cfg->max_seq * half), st((size_t)cfg->max_seq * half);
-    for (int p = 0; p < cfg->max_seq; ++p)
+    const int npos = positions(cfg);
+    std::vector<float> ct((size_t)npos * half), st((size_t)npos * half);
+    for (int p = 0; p < npos; ++p)
       for (int i = 0; i < half; ++i) {
         const double inv_freq = std::pow(cfg->rope_theta, -(2.0 * (double)i) / (double)m->hd);
         const double ang = (double)p * inv_freq;
@@ -706,7 +723,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
 int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
                    float* dev_logits, int32_t* dev_next) {
   if (!m || !tokens || batch <= 0 || batch > m->c.max_batch) return LD_E_INVAL;
-  if (m->pos + 1 > m->c.max_seq) return LD_E_RANGE;
+  if (m->pos + 1 > positions(&m->c)) return LD_E_RANGE;
   if (!tokens_on_device && !tokens_valid(tokens, (size_t)batch, m->c.vocab_size)) return LD_E_INVAL;
   DeviceGuard dg(m->device);
   const int* d_tok = tokens_on_device ? tokens : m->at<int>(m->lay.tok);
@@ -728,7 +745,7 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
 int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host_tokens,
                float* dev_logits, int32_t* dev_next, int32_t all_pos) {
   if (!m || !host_tokens || batch <= 0 || batch > m->c.max_batch || n_tokens <= 0) return LD_E_INVAL;
-  if ((int64_t)m->pos + n_tokens > m->c.max_seq) return LD_E_RANGE;
+  if ((int64_t)m->pos + n_tokens > positions(&m->c)) return LD_E_RANGE;
   if (!tokens_valid(host_tokens, (size_t)batch * n_tokens, m->c.vocab_size)) return LD_E_INVAL;
   DeviceGuard dg(m->device);
   const ld_config& c = m->c;
@@ -736,8 +753,14 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
   const int nc_max = std::max(1, R / batch);   // positions per chunk
   std::vector<int32_t> chunk_tok;
   const int pos0 = m->pos;
-  for (int t0 = 0; t0 < n_tokens; t0 += nc_max) {
-    const int nc = std::min(nc_max, n_tokens - t0);
+  const int ring = m->lay.seq_pad, window = c.max_seq;
+  for (int t0 = 0, nc = 0; t0 < n_tokens; t0 += nc) {
+    // a chunk starting at position p0 overwrites the slots of positions p0 - ring ..;
+    // its earliest row still sees p0 - window + 1 on: at most ring - window + 1
+    // positions once the ring has wrapped, or up to the first slot still in use
+    const int p0 = pos0 + t0;
+    const int safe = std::max(ring - window + 1, ring - p0);
+    nc = std::min(std::min(nc_max, safe), n_tokens - t0);
     const int rows = batch * nc;
     chunk_tok.resize((size_t)rows);
     for (int b = 0; b < batch; ++b)
@@ -764,7 +787,7 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
 int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* tokens,
                 int32_t tokens_on_device, float* dev_logits, int32_t* dev_out) {
   if (!m || !tokens || batch <= 0 || batch > m->c.max_batch || n_steps < 0) return LD_E_INVAL;
-  if ((int64_t)m->pos + n_steps > m->c.max_seq) return LD_E_RANGE;
+  if ((int64_t)m->pos + n_steps > positions(&m->c)) return LD_E_RANGE;
   if (!tokens_on_device && !tokens_valid(tokens, (size_t)batch, m->c.vocab_size)) return LD_E_INVAL;
   if (n_steps == 0) return LD_OK;
   DeviceGuard dg(m->device);
@@ -797,6 +820,10 @@ int ld_kv_reset(ld_model* m) {
 int ld_set_pos(ld_model* m, int32_t new_pos) {
   if (!m) return LD_E_INVAL;
   if (new_pos < 0 || new_pos > m->pos) return LD_E_RANGE;
+  // the cache must still hold the window of new_pos: positions new_pos - max_seq ..
+  // new_pos - 1 (the ring holds m->pos - ring .. m->pos - 1)
+  const int ring = m->lay.seq_pad;
+  if (m->pos > ring && new_pos - m->c.max_seq < m->pos - ring) return LD_E_RANGE;
   m->pos = new_pos;
   return LD_OK;
 }
@@ -937,7 +964,7 @@ const char* ld_strerror(int code) {
   switch (code) {
     case LD_OK: return "ok";
     case LD_E_INVAL: return "invalid argument";
-    case LD_E_RANGE: return "position out of range (max_seq reached)";
+    case LD_E_RANGE: return "position out of range (max_pos reached, or a rewind past the cache)";
     case LD_E_ARENA: return "arena too small or misaligned";
     case LD_E_HIP: return "HIP runtime error";
     case LD_E_NONFINITE: return "non-finite logit or out-of-range device token";

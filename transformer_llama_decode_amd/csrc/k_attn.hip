@@ -171,7 +171,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
       nchunk = std::max(1, std::min(a.seq_pad / kTile, 512 / units));
     } else {
       // about 256 workgroups: one or two tiles each (measured best at the 7B decode shape)
-      const int tiles = (a.pos + a.n_tok + kTile - 1) / kTile;   // longest history among the rows
+      // slots visited by the longest history among the rows
+      const int tiles = (std::min(a.pos + a.n_tok, a.seq_pad) + kTile - 1) / kTile;
       int per = std::max(1, (units * tiles) / 256);
       while ((size_t)units * ((tiles + per - 1) / per) > (size_t)kMaxAttnParts) ++per;
       nchunk = (tiles + per - 1) / per;

@@ -14,8 +14,10 @@
 //    (r < 16) of each 32-key half tile;
 //  * online softmax per query: running max m (the two lanes of a query agree
 //    through one exchange), the exponentials in fp64 rounded to fp32 for the
-//    matrix cores, per-lane partial sums l in fp64; causal masking selects
-//    -inf, so cache entries past a row's history never enter the sums;
+//    matrix cores, per-lane partial sums l in fp64; masking (causality, and the
+//    sliding window past max_seq: keys are cache slots, KvRing maps them to
+//    positions) selects -inf, so entries outside a row's window never enter
+//    the sums;
 //  * O^T += V^T P^T (dims x queries): the probabilities are already in the
 //    B-operand layout (same lane, same key order), V^T's operand is read straight
 //    from the V cache: lane c of output tile t stands for dimension NO*c + t
@@ -25,6 +27,8 @@
 // Scores are fp32 matrix-core sums of fp32 products (relative error ~1e-7 of
 // |q||k|) and O accumulates in fp32; the decode path keeps fp64 sums.  Both are
 // well inside the logits' 1e-4 tolerance (long-prompt parity tests).
+#include <algorithm>
+
 #include "dev_common.hpp"
 #include "ld_internal.hpp"
 
@@ -77,10 +81,12 @@ __global__ void __launch_bounds__(64 * NW) k_attn_mfma(AttnArgs a, int qtiles) {
   const int h = blockIdx.y, z = blockIdx.z;
   const int b = z / qtiles, t0 = (z - b * qtiles) * kQRows;
   const int pos = a.pos_dev != nullptr ? *a.pos_dev : a.pos;
+  const KvRing kr(a.seq_pad, a.window, pos + a.n_tok - 1);
   const int nrows = min(kQRows, a.n_tok - t0);
-  const int kvlen = pos + t0 + nrows;        // history of the last row
+  const int kvlen = min(pos + t0 + nrows, kr.nslots);   // slots the last row visits
   const int ntiles = (kvlen + kKeys - 1) / kKeys;
   const int qpos = pos + t0 + col;           // position of this lane's query row
+  const int lo_q = kr.lo(qpos);
   const size_t head_off = ((size_t)b * a.kvh + h / (a.H / a.kvh)) * (size_t)a.seq_pad * HD;
   const float4* kt = reinterpret_cast<const float4*>(a.kc + head_off);
   const float* vb = a.vc + head_off + NO * col;
@@ -123,8 +129,8 @@ __global__ void __launch_bounds__(64 * NW) k_attn_mfma(AttnArgs a, int qtiles) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j0 + 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key > qpos) s[c][r] = -INFINITY;
+        const int key = j0 + 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);   // cache slot
+        if (!(key < kvlen && kr.visible(key, qpos, lo_q))) s[c][r] = -INFINITY;
         smax = fmaxf(smax, s[c][r]);
       }
     smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
@@ -177,7 +183,7 @@ __global__ void __launch_bounds__(64 * NW) k_attn_mfma(AttnArgs a, int qtiles) {
     double m_all = m_run;
 #pragma unroll
     for (int u = 0; u < NW - 1; ++u) m_all = fmax(m_all, ml_sh[(u * 2) * 64 + lane]);
-    const double s0 = exp(m_run - m_all);   // wave 0 always holds tile 0: m_run is finite
+    const double s0 = m_run == -INFINITY ? 0.0 : exp(m_run - m_all);
     l_half *= s0;
     float fs[NW - 1];
 #pragma unroll
@@ -216,7 +222,8 @@ __global__ void __launch_bounds__(64 * NW) k_attn_mfma(AttnArgs a, int qtiles) {
 }  // namespace
 
 bool attention_prefill_supported(const AttnArgs& a) {
-  return a.n_tok >= kQRows && a.hd % 32 == 0 && a.hd <= 256 && a.seq_pad % kKeys == 0;
+  // (head dim 256 would keep 128 fp32 Q^T and 128 O^T registers per lane and spill)
+  return a.n_tok >= kQRows && a.hd % 32 == 0 && a.hd <= 224 && a.seq_pad % kKeys == 0;
 }
 
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s) {
@@ -224,7 +231,7 @@ hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const int qtiles = (a.n_tok + kQRows - 1) / kQRows;
   // waves per workgroup: enough to split the longest history a few ways
-  const int span = a.pos_dev != nullptr ? a.seq_pad : a.pos + a.n_tok;
+  const int span = a.pos_dev != nullptr ? a.seq_pad : std::min(a.pos + a.n_tok, a.seq_pad);
   const int tiles = (span + kKeys - 1) / kKeys;
   // (four waves of head_dim >= 192 would need more than 64 KB of LDS for the merge)
   const int nw = tiles >= 4 && a.hd < 192 ? 4 : (tiles >= 2 ? 2 : 1);
@@ -239,7 +246,7 @@ hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s) {
     break;
   switch (a.hd) {
     LD_ATTN_MFMA_CASE(32) LD_ATTN_MFMA_CASE(64) LD_ATTN_MFMA_CASE(96) LD_ATTN_MFMA_CASE(128)
-    LD_ATTN_MFMA_CASE(160) LD_ATTN_MFMA_CASE(192) LD_ATTN_MFMA_CASE(224) LD_ATTN_MFMA_CASE(256)
+    LD_ATTN_MFMA_CASE(160) LD_ATTN_MFMA_CASE(192) LD_ATTN_MFMA_CASE(224)
     default: return hipErrorInvalidValue;
   }
 #undef LD_ATTN_MFMA_CASE

@@ -196,9 +196,9 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           if (sec == 0)
             a.q_out[(size_t)row * d + c] = out;
           else if (sec == 1)
-            a.kc[head_off + ktile_index(p, ii, hd)] = out;
+            a.kc[head_off + ktile_index(kv_slot(p, a.seq_pad), ii, hd)] = out;
           else
-            a.vc[head_off + (size_t)p * hd + ii] = out;
+            a.vc[head_off + (size_t)kv_slot(p, a.seq_pad) * hd + ii] = out;
         }
   } else if (EPI == EPI_SWIGLU) {
     static_assert(EPI != EPI_SWIGLU || NT == 2, "SwiGLU pairs W1/W3 tiles");
@@ -474,11 +474,13 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
         a.q_out[(size_t)r * d + c] = y0;
         a.q_out[(size_t)r * d + c + 1] = y1;
       } else if (sec == 1) {
-        a.kc[head_off + ktile_index(p, ii, hd)] = y0;
-        a.kc[head_off + ktile_index(p, ii + 1, hd)] = y1;
+        const int slot = kv_slot(p, a.seq_pad);
+        a.kc[head_off + ktile_index(slot, ii, hd)] = y0;
+        a.kc[head_off + ktile_index(slot, ii + 1, hd)] = y1;
       } else {
-        a.vc[head_off + (size_t)p * hd + ii] = y0;
-        a.vc[head_off + (size_t)p * hd + ii + 1] = y1;
+        const size_t vrow = (size_t)kv_slot(p, a.seq_pad) * hd;
+        a.vc[head_off + vrow + ii] = y0;
+        a.vc[head_off + vrow + ii + 1] = y1;
       }
     }
   } else if (EPI == EPI_SWIGLU) {

@@ -321,10 +321,11 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         a.q_out[c + 1] = y1;
       } else if (sec == 1) {
         float* kh = a.kc + (size_t)h * a.seq_pad * hd;
-        kh[ktile_index(pos, ii, hd)] = y0;
-        kh[ktile_index(pos, ii + 1, hd)] = y1;
+        const int slot = kv_slot(pos, a.seq_pad);
+        kh[ktile_index(slot, ii, hd)] = y0;
+        kh[ktile_index(slot, ii + 1, hd)] = y1;
       } else {
-        float* vrow = a.vc + ((size_t)h * a.seq_pad + pos) * hd;
+        float* vrow = a.vc + ((size_t)h * a.seq_pad + kv_slot(pos, a.seq_pad)) * hd;
         vrow[ii] = y0;
         vrow[ii + 1] = y1;
       }

@@ -94,13 +94,14 @@ struct AttnArgs {
   float* out;          // [rows][d]
   double* part;        // partial (o[hd], m, l) per (row, head, chunk)
   int* ticket;         // chunks finished per (row, head); zero between launches
-  int rows, n_tok, pos, d, H, hd, seq_pad, bmax;
+  int rows, n_tok, pos, d, H, hd, seq_pad, bmax;   // seq_pad: KV slots per sequence (the ring)
+  int window;          // positions a query sees: q - window + 1 .. q (max_seq)
   int kvh;             // key/value heads; query head h reads key/value head h / (H / kvh)
   const int* pos_dev;  // when set, the position is read from device memory instead of pos,
                        // and the chunk count is fixed by the cache length (graph replays)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
-// prompts of 32 or more rows on the matrix cores (head_dim a multiple of 32, at most 256)
+// prompts of 32 or more rows on the matrix cores (head_dim a multiple of 32, at most 224)
 bool attention_prefill_supported(const AttnArgs& a);
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s);
 

@@ -15,7 +15,7 @@ from .configs import ModelConfig
 def _cfg_struct(cfg: ModelConfig):
     return LdConfig(cfg.dim, cfg.n_layers, cfg.n_heads, cfg.hidden_dim, cfg.vocab_size, cfg.max_seq,
                     cfg.max_batch, int(cfg.tied), int(cfg.n_kv_heads or 0), int(bool(cfg.weight_bf16)),
-                    float(cfg.rope_theta), float(cfg.norm_eps))
+                    int(cfg.max_pos or 0), float(cfg.rope_theta), float(cfg.norm_eps))
 
 
 def arena_bytes(cfg: ModelConfig) -> int:
@@ -133,6 +133,9 @@ class LlamaDecoder:
 
     def set_pos(self, p):
         check(self.L.ld_set_pos(self._h, p), "ld_set_pos")
+
+    def set_pos_rc(self, p):
+        return self.L.ld_set_pos(self._h, p)
 
     @property
     def pos(self):

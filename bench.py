@@ -99,6 +99,20 @@ def cpu_baseline(w, n_steps):
     }
 
 
+COUNTER_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- "
+    "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- "
+    "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o f -- "
+    "python -u bench.py --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o w -- "
+    "python -u bench.py --copy-calibration",
+    "python bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write "
+    "gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
+]
+
+
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_json, out_txt):
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the 7B decode
     bench, and of the plain 2 GiB copy of --copy-calibration) into HBM bytes per
@@ -143,6 +157,9 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out
     with open(out_json, "w") as fh:
         json.dump(rec, fh, indent=1)
     with open(out_txt, "w") as fh:
+        fh.write("HBM traffic per kernel launch from rocprofv3 counters, 7B-shape decode at batch 1.\n"
+                 "commands (from the repository root, on the MI355X box; each pass a run of its own):\n"
+                 + "".join("  %s\n" % c for c in COUNTER_COMMANDS) + "\n")
         fh.write("copy calibration: a 2 GiB device copy reads FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB "
                  "-> scale fetch x%.4f, write x%.4f\n" % (f_copy / 1024, w_copy / 1024, k_fetch, k_write))
         fh.write("\n".join(lines) + "\n")

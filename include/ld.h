@@ -22,7 +22,7 @@
  * Conventions for every call:
  *  - Return LD_OK (0) or a negative LD_E_* code.  On error no state changes.
  *  - `hip_stream` passed to ld_model_init is used for every later call; all
- *    calls except ld_model_init, ld_read_weights, ld_status and
+ *    calls except ld_model_init, ld_read_weights, ld_weights_checksum, ld_status and
  *    ld_profile_read are asynchronous on that stream and never allocate.
  *  - Device memory is owned by the caller: one arena of ld_arena_bytes() bytes
  *    (256-byte aligned) holds weights, rotary tables, KV cache and scratch.
@@ -157,6 +157,15 @@ int ld_get_pos(const ld_model* m, int32_t* pos);
  * numbering, logical row-major layout) to host memory as fp32 (bfloat16
  * weights widened exactly).  Synchronous. */
 int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, float* host_out);
+
+/* Checksum of every weight matrix as held on the device: the sum, modulo 2^64,
+ * of the 32-bit patterns of all elements of E, Wq, Wk, Wv, Wo, W1, W2, W3 of
+ * every layer and the untied classifier (bfloat16 elements widened to fp32
+ * first).  Order-free, so a reference computes it from the tensors in any
+ * layout; equal sums mean the generator was reproduced bit for bit (the
+ * survey's generator-identity check; norm gains are excluded).  Synchronous:
+ * waits for the model's stream. */
+int ld_weights_checksum(ld_model* m, uint64_t* sum);
 
 /* Wait for the stream and report a device-side error raised since the last
  * call (LD_E_NONFINITE), then clear it. */

@@ -90,6 +90,11 @@ def test_weights_on_device_are_the_generator_values(dev, cfg, seed):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), sid
         if not cfg.weight_bf16:
             assert np.array_equal(want, O.synth_normal(seed, sid, 0, n)), sid
+    # the library's whole-model checksum: sum of the elements' 32-bit patterns mod 2^64
+    want_sum = 0
+    for sid in ids:
+        want_sum = (want_sum + int(om.tensor(sid).view(np.uint32).astype(np.uint64).sum(dtype=np.uint64))) % 2**64
+    assert gm.weights_checksum() == want_sum
     gm.close()
 
 

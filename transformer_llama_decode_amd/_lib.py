@@ -22,7 +22,7 @@ LD_K_QKV, LD_K_ATTN, LD_K_WO, LD_K_W13, LD_K_W2, LD_K_CLS = range(6)
 # every entry point declared in include/ld.h
 EXPORTS = [
     "ld_arena_bytes", "ld_model_init", "ld_prefill", "ld_decode_step", "ld_generate", "ld_kv_reset",
-    "ld_set_pos", "ld_get_pos", "ld_read_weights", "ld_status", "ld_profile",
+    "ld_set_pos", "ld_get_pos", "ld_read_weights", "ld_weights_checksum", "ld_status", "ld_profile",
     "ld_profile_read", "ld_synth_prompt", "ld_model_free", "ld_strerror",
 ]
 
@@ -62,6 +62,7 @@ def lib():
         L.ld_set_pos.argtypes = [vp, i32]
         L.ld_get_pos.argtypes = [vp, C.POINTER(i32)]
         L.ld_read_weights.argtypes = [vp, i64, u64, u64, C.POINTER(C.c_float)]
+        L.ld_weights_checksum.argtypes = [vp, C.POINTER(u64)]
         L.ld_status.argtypes = [vp]
         L.ld_profile.argtypes = [vp, i32, i32]
         L.ld_profile_read.argtypes = [vp, i32, C.POINTER(C.c_double), C.POINTER(i64)]

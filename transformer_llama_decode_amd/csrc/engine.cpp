@@ -109,6 +109,7 @@ void make_layout(const ld_config* c, Layout* L) {
   L->tok = take(R * 4);
   L->next = take(R * 4);
   L->err = take(4);
+  L->csum = take(8);
   L->pos_dev = take(2 * 4);
   L->gen = take(P * B * 4);
   L->total = off;
@@ -890,6 +891,28 @@ int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, 
     const uint32_t u = (uint32_t)raw[k] << 16;
     std::memcpy(host_out + k, &u, sizeof u);
   }
+  return LD_OK;
+}
+
+int ld_weights_checksum(ld_model* m, uint64_t* sum) {
+  if (!m || !sum) return LD_E_INVAL;
+  const ld_config& c = m->c;
+  DeviceGuard dg(m->device);
+  const size_t d = c.dim, f = c.hidden_dim, V = c.vocab_size, kvd = m->kvd;
+  unsigned long long* acc = m->at<unsigned long long>(m->lay.csum);
+  LD_TRY_HIP(hipMemsetAsync(acc, 0, sizeof *acc, m->stream));
+  LD_TRY_HIP(launch_bits_sum(m->arena + m->lay.E, V * d, m->bf16, acc, m->stream));
+  for (int l = 0; l < c.n_layers; ++l) {
+    LD_TRY_HIP(launch_bits_sum(m->wlayer(l, m->lay.o_wqkv), (d + 2 * kvd) * d, m->bf16, acc, m->stream));
+    LD_TRY_HIP(launch_bits_sum(m->wlayer(l, m->lay.o_wo), d * d, m->bf16, acc, m->stream));
+    LD_TRY_HIP(launch_bits_sum(m->wlayer(l, m->lay.o_w13), 2 * f * d, m->bf16, acc, m->stream));
+    LD_TRY_HIP(launch_bits_sum(m->wlayer(l, m->lay.o_w2), d * f, m->bf16, acc, m->stream));
+  }
+  if (!c.tied_classifier) LD_TRY_HIP(launch_bits_sum(m->arena + m->lay.Wcls, V * d, m->bf16, acc, m->stream));
+  unsigned long long h = 0;
+  LD_TRY_HIP(hipMemcpyAsync(&h, acc, sizeof h, hipMemcpyDeviceToHost, m->stream));
+  LD_TRY_HIP(hipStreamSynchronize(m->stream));
+  *sum = (uint64_t)h;
   return LD_OK;
 }
 

@@ -99,6 +99,19 @@ __global__ void k_fill(float* p, float v, size_t n) {
     p[i] = v;
 }
 
+// Sum of 32-bit element patterns, modulo 2^64 (integer adds: order-free, so
+// the device-wide atomic accumulation is deterministic).
+template <bool BF>
+__global__ void __launch_bounds__(256) k_bits_sum(const void* p, size_t n, unsigned long long* out) {
+  unsigned long long acc = 0;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    acc += BF ? (unsigned long long)((uint32_t)static_cast<const uint16_t*>(p)[i] << 16)
+              : (unsigned long long)static_cast<const uint32_t*>(p)[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) atomicAdd(out, acc);
+}
+
 __global__ void k_set_int(int* p, int v) {
   if (threadIdx.x == 0) *p = v;
 }
@@ -132,6 +145,17 @@ hipError_t launch_argmax_finalize(const float* part_val, const int* part_idx, in
 
 hipError_t launch_set_int(int* p, int v, hipStream_t s) {
   hipLaunchKernelGGL(k_set_int, dim3(1), dim3(64), 0, s, p, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_bits_sum(const void* p, size_t n, bool bf16, unsigned long long* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (bf16)
+    hipLaunchKernelGGL(k_bits_sum<true>, dim3((unsigned)blocks), dim3(256), 0, s, p, n, out);
+  else
+    hipLaunchKernelGGL(k_bits_sum<false>, dim3((unsigned)blocks), dim3(256), 0, s, p, n, out);
   return hipGetLastError();
 }
 

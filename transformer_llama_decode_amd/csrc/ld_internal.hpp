@@ -44,6 +44,7 @@ struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
   size_t x, xn, q, att, g, attn_part, attn_ticket, sk_ws, sk_ticket, arg_val, arg_idx, tok, next, err;
+  size_t csum;         // one 64-bit accumulator of ld_weights_checksum
   size_t pos_dev, gen;
   size_t total;
   int rows;            // R: activation rows per forward pass
@@ -164,6 +165,8 @@ hipError_t launch_argmax_finalize(const float* part_val, const int* part_idx, in
                                   int row_stride, int row_offset, int* next, int* next2,
                                   const FinalizeRing* ring, hipStream_t s);
 hipError_t launch_set_int(int* p, int v, hipStream_t s);
+// *out += sum of the 32-bit patterns of n elements (fp32, or bfloat16 widened)
+hipError_t launch_bits_sum(const void* p, size_t n, bool bf16, unsigned long long* out, hipStream_t s);
 hipError_t launch_fill(float* p, float v, size_t n, hipStream_t s);
 
 }  // namespace ld

@@ -149,6 +149,11 @@ class LlamaDecoder:
                                      out.ctypes.data_as(C.POINTER(C.c_float))), "ld_read_weights")
         return out
 
+    def weights_checksum(self):
+        v = C.c_uint64(0)
+        check(self.L.ld_weights_checksum(self._h, C.byref(v)), "ld_weights_checksum")
+        return v.value
+
     def status(self):
         return self.L.ld_status(self._h)
 

@@ -43,28 +43,61 @@ __device__ __forceinline__ float4 load_w4(const void* W, size_t idx) {
   return *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
 }
 
-// Global -> register loads of one K step: BM x 32 values of A, BN x 32 of W
-// (8 float4 per row); rows past M / N read as zero.  BF: the source is bfloat16.
+// Global -> register loads of one K step: BM x 32 values of A, BN x 32 of W;
+// rows past M / N read as zero.  fp32: 8 16-byte loads per row, slot i holds
+// k 4c..4c+3.  bfloat16 (BF): 4 16-byte loads of 8 weights per row, widened
+// into slots 2i and 2i+1 (k 8c..8c+7), so a row is still 64 contiguous bytes
+// per 4 lanes rather than 8-byte pieces.
 template <int ROWS, int NTHR, bool BF, int L>
 __device__ __forceinline__ void tile_gload(float4 (&r)[L], const void* __restrict__ src, int row0,
                                            int nrows, int K, int k0, int tid) {
+  if constexpr (BF) {
+    static_assert(L % 2 == 0, "two widened slots per bfloat16 load");
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int idx = tid + i * NTHR;
-    const int row = idx >> 3, c4 = idx & 7, g = row0 + row;
-    if (idx < ROWS * 8 && g < nrows)
-      r[i] = load_w4<BF>(src, (size_t)g * K + k0 + c4 * 4);
-    else
-      r[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < L / 2; ++i) {
+      const int idx = tid + i * NTHR;
+      const int row = idx >> 2, c8 = idx & 3, g = row0 + row;
+      if (idx < ROWS * 4 && g < nrows) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)g * K +
+                                                        k0 + c8 * 8);
+        r[2 * i] = bf16x4(make_uint2(u.x, u.y));
+        r[2 * i + 1] = bf16x4(make_uint2(u.z, u.w));
+      } else {
+        r[2 * i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        r[2 * i + 1] = r[2 * i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int idx = tid + i * NTHR;
+      const int row = idx >> 3, c4 = idx & 7, g = row0 + row;
+      if (idx < ROWS * 8 && g < nrows)
+        r[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + (size_t)g * K + k0 + c4 * 4);
+      else
+        r[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
 }
 
-template <int ROWS, int NTHR, int L>
+template <int ROWS, int NTHR, bool BF, int L>
 __device__ __forceinline__ void tile_sstore(const float4 (&r)[L], float* dst, int tid) {
+  if constexpr (BF) {
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int idx = tid + i * NTHR;
-    if (idx < ROWS * 8) *reinterpret_cast<float4*>(&dst[(idx >> 3) * LDS_STRIDE + (idx & 7) * 4]) = r[i];
+    for (int i = 0; i < L / 2; ++i) {
+      const int idx = tid + i * NTHR;
+      if (idx < ROWS * 4) {
+        float* p = &dst[(idx >> 2) * LDS_STRIDE + (idx & 3) * 8];
+        *reinterpret_cast<float4*>(p) = r[2 * i];
+        *reinterpret_cast<float4*>(p + 4) = r[2 * i + 1];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int idx = tid + i * NTHR;
+      if (idx < ROWS * 8) *reinterpret_cast<float4*>(&dst[(idx >> 3) * LDS_STRIDE + (idx & 7) * 4]) = r[i];
+    }
   }
 }
 
@@ -99,8 +132,8 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 
   tile_gload<BM, NTHR, false>(ra, a.A, m0, M, K, 0, tid);
   tile_gload<BN, NTHR, BF>(rb, a.W, n0, N, K, 0, tid);
-  tile_sstore<BM, NTHR>(ra, As[0], tid);
-  tile_sstore<BN, NTHR>(rb, Bs[0], tid);
+  tile_sstore<BM, NTHR, false>(ra, As[0], tid);
+  tile_sstore<BN, NTHR, BF>(rb, Bs[0], tid);
   __syncthreads();
   int cur = 0;
   const int arow = wm * MT * 32 + (lane & 31), brow = wn * NT * 32 + (lane & 31);
@@ -144,8 +177,8 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           }
     }
     if (more) {
-      tile_sstore<BM, NTHR>(ra, As[cur ^ 1], tid);
-      tile_sstore<BN, NTHR>(rb, Bs[cur ^ 1], tid);
+      tile_sstore<BM, NTHR, false>(ra, As[cur ^ 1], tid);
+      tile_sstore<BN, NTHR, BF>(rb, Bs[cur ^ 1], tid);
     }
     __syncthreads();
     cur ^= 1;

@@ -113,7 +113,15 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous
+  // range of tiles, row blocks of one W column block next to each other, so a
+  // W tile is fetched into one XCD's L2 and reused there
+  const int nbx = a.tiles_n, nby = a.tiles_m, total = nbx * nby;
+  const int per = (total + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= total) return;
+  const int bx = t / nby, by = t - bx * nby;
+  const int m0 = by * BM, n0 = bx * BN;
   const int M = a.M, N = a.N, K = a.K;
   // QKV epilogue position, read at the start so the load overlaps the main loop
   const int pos0 = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
@@ -246,7 +254,7 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           a.g_out[(size_t)row * a.f + fcol] = swiglu(val(mt, 0, j), val(mt, NT - 1, j));
       }
   } else {  // EPI_CLS
-    const int nparts = gridDim.x * WN, part = blockIdx.x * WN + wn;
+    const int nparts = nbx * WN, part = bx * WN + wn;
     bool bad = false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -612,11 +620,14 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     bm = 64;
   else
     bm = 32;
-  dim3 grid(nb, (a.M + bm - 1) / bm);
+  GemmArgs g = a;
+  g.tiles_n = nb;
+  g.tiles_m = (a.M + bm - 1) / bm;
+  dim3 grid(((g.tiles_n * g.tiles_m + 7) / 8) * 8);
   if (nparts) *nparts = nb * 2;
 #define LD_GEMM_LAUNCH1(WM, MT, THR, CARRY, BF)                                                  \
   hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, CARRY, BF>), grid, dim3(THR), 0, s, a.ev_start, \
-                        a.ev_stop, 0, a)
+                        a.ev_stop, 0, g)
 #define LD_GEMM_LAUNCH(WM, MT, THR)                                      \
   if (a.bf16) {                                                          \
     if (a.carry) LD_GEMM_LAUNCH1(WM, MT, THR, true, true);               \

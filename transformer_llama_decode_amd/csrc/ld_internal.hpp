@@ -138,6 +138,7 @@ struct GemmArgs {
   // launches); nullptr ws keeps every tile in one workgroup
   double* ws;
   int* tickets;
+  int tiles_n, tiles_m;   // LDS-tiled kernel: output tiles along N and M (set by its launcher)
 };
 // capacity of the split-K workspace: tiles that may be split, slices per tile, bytes
 constexpr int kSkMaxTiles = 256;

@@ -99,18 +99,16 @@ def cpu_baseline(w, n_steps):
     }
 
 
-COUNTER_COMMANDS = [
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- "
-    "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- "
-    "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline",
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o f -- "
-    "python -u bench.py --copy-calibration",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o w -- "
-    "python -u bench.py --copy-calibration",
-    "python bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write "
-    "gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
-]
+def counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """The rocprofv3 passes a traffic summary comes from (each counter in a run of its own)."""
+    run = "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline"
+    cal = "python -u bench.py --copy-calibration"
+    return ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o f -- %s" % (fetch_dir, run),
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o w -- %s" % (write_dir, run),
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o f -- %s" % (copy_fetch_dir, cal),
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o w -- %s" % (copy_write_dir, cal),
+            "python bench.py --summarize-counters %s %s %s %s"
+            % (fetch_dir, write_dir, copy_fetch_dir, copy_write_dir)]
 
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_json, out_txt):
@@ -158,8 +156,9 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out
         json.dump(rec, fh, indent=1)
     with open(out_txt, "w") as fh:
         fh.write("HBM traffic per kernel launch from rocprofv3 counters, 7B-shape decode at batch 1.\n"
-                 "commands (from the repository root, on the MI355X box; each pass a run of its own):\n"
-                 + "".join("  %s\n" % c for c in COUNTER_COMMANDS) + "\n")
+                 "commands (from the repository root, on an MI355X; each pass a run of its own):\n"
+                 + "".join("  %s\n" % c for c in counter_commands(fetch_dir, write_dir, copy_fetch_dir,
+                                                                   copy_write_dir)) + "\n")
         fh.write("copy calibration: a 2 GiB device copy reads FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB "
                  "-> scale fetch x%.4f, write x%.4f\n" % (f_copy / 1024, w_copy / 1024, k_fetch, k_write))
         fh.write("\n".join(lines) + "\n")
@@ -198,8 +197,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs the decode path on a single "
-              "MI355X (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -162,8 +162,8 @@ int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, 
  * of the 32-bit patterns of all elements of E, Wq, Wk, Wv, Wo, W1, W2, W3 of
  * every layer and the untied classifier (bfloat16 elements widened to fp32
  * first).  Order-free, so a reference computes it from the tensors in any
- * layout; equal sums mean the generator was reproduced bit for bit (the
- * survey's generator-identity check; norm gains are excluded).  Synchronous:
+ * layout; equal sums mean the generator was reproduced bit for bit (norm
+ * gains are excluded).  Synchronous:
  * waits for the model's stream. */
 int ld_weights_checksum(ld_model* m, uint64_t* sum);
 

@@ -146,3 +146,26 @@ def test_window_arena_adds_the_ring_slack_and_rotary_rows(L):
     n2 = C.c_size_t(0)
     assert L.ld_arena_bytes(C.byref(_cfg(replace(m, max_pos=100))), C.byref(n2)) == 0
     assert n2.value == n0.value                                      # max_pos = max_seq: no window
+
+
+def test_model_init_rejects_a_small_or_misaligned_arena_before_touching_it(L):
+    """checked on the host before any device call: the pointers are never dereferenced"""
+    n = C.c_size_t(0)
+    c = _cfg(TINY)
+    assert L.ld_arena_bytes(C.byref(c), C.byref(n)) == 0
+    h = C.c_void_p()
+    fake = C.c_void_p(1 << 40)                       # 256-byte aligned, never dereferenced
+    assert L.ld_model_init(C.byref(c), 0, fake, n.value - 256, None, C.byref(h)) == _lib.LD_E_ARENA
+    assert L.ld_model_init(C.byref(c), 0, C.c_void_p((1 << 40) + 64), n.value, None, C.byref(h)) == _lib.LD_E_ARENA
+    assert not h.value
+
+
+def test_calls_on_a_null_handle_are_rejected(L):
+    i32 = C.c_int32()
+    u64 = C.c_uint64()
+    assert L.ld_get_pos(None, C.byref(i32)) == _lib.LD_E_INVAL
+    assert L.ld_set_pos(None, 0) == _lib.LD_E_INVAL
+    assert L.ld_weights_checksum(None, C.byref(u64)) == _lib.LD_E_INVAL
+    assert L.ld_generate(None, 1, 1, None, 0, None, None) == _lib.LD_E_INVAL
+    assert L.ld_status(None) == _lib.LD_E_INVAL
+    assert L.ld_read_weights(None, 0, 0, 1, None) == _lib.LD_E_INVAL

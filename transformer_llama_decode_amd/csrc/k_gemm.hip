@@ -627,24 +627,30 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   g.tiles_m = (a.M + bm - 1) / bm;
   dim3 grid(((g.tiles_n * g.tiles_m + 7) / 8) * 8);
   if (nparts) *nparts = nb * 2;
-#define LD_GEMM_LAUNCH1(WM, MT, THR, CARRY, BF)                                                  \
-  hipExtLaunchKernelGGL((k_gemm<WM, 2, MT, 2, EPI, CARRY, BF>), grid, dim3(THR), 0, s, a.ev_start, \
+#define LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, CARRY, BF)                                            \
+  hipExtLaunchKernelGGL((k_gemm<WM, WN, MT, NT, EPI, CARRY, BF>), grid, dim3(THR), 0, s, a.ev_start, \
                         a.ev_stop, 0, g)
-#define LD_GEMM_LAUNCH(WM, MT, THR)                                      \
-  if (a.bf16) {                                                          \
-    if (a.carry) LD_GEMM_LAUNCH1(WM, MT, THR, true, true);               \
-    else LD_GEMM_LAUNCH1(WM, MT, THR, false, true);                      \
-  } else {                                                               \
-    if (a.carry) LD_GEMM_LAUNCH1(WM, MT, THR, true, false);              \
-    else LD_GEMM_LAUNCH1(WM, MT, THR, false, false);                     \
+#define LD_GEMM_LAUNCH(WM, WN, MT, NT, THR)                                      \
+  if (a.bf16) {                                                                  \
+    if (a.carry) LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, true, true);               \
+    else LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, false, true);                      \
+  } else {                                                                       \
+    if (a.carry) LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, true, false);              \
+    else LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, false, false);                     \
   }
   if (bm == 128) {
-    LD_GEMM_LAUNCH(4, 1, 512)   // 8 waves of 32 x 64: two waves per SIMD hide each other's waits
-                                // (7B prompt W1/W3 1044 -> 973 us against 4 waves of 64 x 64)
+    LD_GEMM_LAUNCH(4, 2, 1, 2, 512)   // 8 waves of 32 x 64: two waves per SIMD hide each other's waits
+                                      // (7B prompt W1/W3 1044 -> 973 us against 4 waves of 64 x 64)
   } else if (bm == 64) {
-    LD_GEMM_LAUNCH(2, 1, 256)
+    if constexpr (EPI == EPI_QKV || EPI == EPI_RESID) {
+      // 8 waves of 32 x 32 (SwiGLU pairs need 64-column wave tiles; the classifier's
+      // arg-max partials are sized for two per 128 columns)
+      LD_GEMM_LAUNCH(2, 4, 1, 1, 512)
+    } else {
+      LD_GEMM_LAUNCH(2, 2, 1, 2, 256)
+    }
   } else {
-    LD_GEMM_LAUNCH(1, 1, 128)
+    LD_GEMM_LAUNCH(1, 2, 1, 2, 128)
   }
 #undef LD_GEMM_LAUNCH
 #undef LD_GEMM_LAUNCH1

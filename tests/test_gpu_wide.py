@@ -7,7 +7,9 @@ the classifier [32000 x 4096], the split-K MFMA GEMMs with fp64 carries and the
 matrix-core prompt attention at head dim 128.  Every logit of a 40-token prompt
 and of 4 decode steps after it is compared with the oracle, for fp32 weights
 with multi-head attention and for bfloat16 weights with 8 key/value heads, and
-one layer run past max_seq over a wrapped ring.
+one layer run past max_seq over a wrapped ring.  A 2048-wide layer run as a
+batch of sequences takes the small-problem GEMM with 32-wide tiles, K split
+over workgroups and fp64 carries.
 """
 import sys
 from dataclasses import replace
@@ -110,4 +112,46 @@ def test_seven_b_shapes_past_max_seq_every_logit(dev):
         assert r >= 0
         assert_logits(gpu_dec[i], ref, "decode pos %d" % (P + i))
         assert_token(feed[i + 1], ref, "decode pos %d" % (P + i))
+    om.close()
+
+
+# 2048 wide: fp64 carries in the matrix-core sums; at 4 x 8 rows (and 4 in decode)
+# the Q/K/V GEMM takes 192 tiles of 32 x 32 in one K slice each (with 4 key/value
+# heads: 96 tiles, K split over 6 workgroups), Wo and W2 64 such tiles with K split
+# over 8 workgroups
+MID_BATCH = ModelConfig(dim=2048, n_layers=1, n_heads=16, hidden_dim=5632, vocab_size=4096, max_seq=32,
+                        max_batch=4, tied=False)
+
+
+@pytest.mark.parametrize("cfg,seed", [(MID_BATCH, 84), (replace(MID_BATCH, weight_bf16=True, n_kv_heads=4), 85)])
+def test_batched_split_k_with_carries_every_logit(dev, cfg, seed):
+    from transformer_llama_decode_amd.model import LlamaDecoder
+    _say("2048-wide batch", cfg)
+    B, P, D = cfg.max_batch, 8, 3
+    gm = LlamaDecoder(cfg, seed)
+    prompts = np.stack([O.synth_prompt(seed, b, P, 3, cfg.vocab_size) for b in range(B)])
+    allp = torch.empty((B, P, cfg.vocab_size), dtype=torch.float32, device=dev)
+    nxt = gm.prefill(prompts, logits=allp, all_pos=True)
+    allp = allp.cpu().numpy()
+    feed = [nxt.cpu().numpy().astype(np.int32)]
+    dec = []
+    lg = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device=dev)
+    for i in range(D):
+        t = gm.decode_step(feed[-1], logits=lg).cpu().numpy().astype(np.int32)
+        dec.append(lg.cpu().numpy().copy())
+        feed.append(t)
+    gm.close()
+    om = O.OracleModel(cfg, seed, nthreads=16)
+    for b in range(B):
+        st = om.new_state()
+        for p in range(P):
+            r, ref = om.forward(st, int(prompts[b, p]), p)
+            assert r >= 0
+            assert_logits(allp[b, p], ref, "seq %d prefill pos %d" % (b, p))
+        assert_token(int(feed[0][b]), ref, "seq %d prefill next" % b)
+        for i in range(D):
+            r, ref = om.forward(st, int(feed[i][b]), P + i)
+            assert r >= 0
+            assert_logits(dec[i][b], ref, "seq %d decode pos %d" % (b, P + i))
+            assert_token(int(feed[i + 1][b]), ref, "seq %d decode pos %d" % (b, P + i))
     om.close()

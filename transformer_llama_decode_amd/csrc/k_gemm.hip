@@ -289,10 +289,11 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Split-K variant for small problems (the layer GEMMs of batched decode): a
-// workgroup of 8 waves owns a 32 x 64 output tile and a slice of K (grid.z
-// slices per tile when the tiles alone would leave most CUs idle), and the
-// waves split the slice between them.  The slice is walked in chunks of kc <= 320: the workgroup stages the chunk's 32
-// A rows and 64 W rows in LDS with row-contiguous 16-byte loads (each wave
+// workgroup of 8 waves owns a 32 x BN output tile (BN = 64 or 32) and a slice of
+// K (grid.z slices per tile when the tiles alone would leave most CUs idle), and
+// the waves split the slice between them.  The slice is walked in chunks of
+// kc <= 320: the workgroup stages the chunk's 32 A rows and BN W rows in LDS with
+// row-contiguous 16-byte loads (each wave
 // instruction reads 1 KiB of consecutive memory; loading straight into the MFMA
 // operand layout would touch 32 rows, i.e. 32 cache lines, per instruction and
 // measured ~4x slower), the next chunk's loads are issued before the current
@@ -305,8 +306,6 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 constexpr int SK_WAVES = 8;
 constexpr int SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_KC = 320;   // largest K chunk staged at once
-constexpr int SK_ROWS = 96;  // 32 A rows + 64 W rows
-constexpr int SK_PER_THREAD = (SK_ROWS * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS;   // float4 slots
 
 template <bool CARRY>
 struct SkAcc {
@@ -317,23 +316,30 @@ struct SkAcc<false> {
   typedef float T;
 };
 
-// LDS bytes for chunk length kc
-size_t sk_lds_bytes(int kc, bool carry) {
-  const size_t stage = (size_t)SK_ROWS * (kc + 4) * sizeof(float);
-  const size_t red = (size_t)SK_WAVES * 2 * 16 * 64 * (carry ? 8 : 4);
+// LDS bytes for chunk length kc and tile width bn
+size_t sk_lds_bytes(int kc, bool carry, int bn) {
+  const size_t stage = (size_t)(32 + bn) * (kc + 4) * sizeof(float);
+  const size_t red = (size_t)SK_WAVES * (bn / 32) * 16 * 64 * (carry ? 8 : 4);
   return stage > red ? stage : red;
 }
 
-template <int EPI, bool CARRY, bool BF>
+template <int EPI, bool CARRY, bool BF, int BN>
 __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int kz) {
   typedef typename SkAcc<CARRY>::T PT;
+  constexpr int NACC = BN / 32;                  // 32 x 32 accumulators per wave
+  constexpr int TE = NACC * 1024;                // elements of the output tile
+  constexpr int ROWS = 32 + BN;                  // staged rows: 32 of A, BN of W
+  constexpr int PER_THREAD = (ROWS * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS;   // float4 slots
+  static_assert(BN == 32 || BN == 64, "tile width");
+  static_assert(EPI != EPI_SWIGLU || BN == 64, "SwiGLU pairs W1 and W3 blocks of 32 rows in one tile");
+  static_assert(EPI != EPI_CLS || BN == 64, "arg-max partials: one lane per column of a 64-wide tile");
   extern __shared__ char sk_smem[];
-  float* stg = reinterpret_cast<float*>(sk_smem);   // [96][kc + 4] while in the K loop
-  PT* red = reinterpret_cast<PT*>(sk_smem);         // [8][2 tiles][16 regs][64 lanes] afterwards
+  float* stg = reinterpret_cast<float*>(sk_smem);   // [ROWS][kc + 4] while in the K loop
+  PT* red = reinterpret_cast<PT*>(sk_smem);         // [8][NACC][16 regs][64 lanes] afterwards
   constexpr int KW = SK_WAVES;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = a.M, N = a.N, K = a.K;
-  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 64;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * BN;
   const int ks = gridDim.z, kbeg = blockIdx.z * kz, kend = min(K, kbeg + kz);   // this K slice
   // QKV epilogue position, read at the start so the load overlaps the main loop
   const int pos0 = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
@@ -343,13 +349,13 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   // operands the epilogue reads, fetched now so they arrive during the K loop:
   // residual elements (thread handles outputs e = tid + i * SK_THREADS) and the
   // rotary cos / sin of its q / k pairs (pairs e = tid + i * SK_THREADS)
-  constexpr int RES_PER = 32 * 64 / SK_THREADS, PAIR_PER = 32 * 32 / SK_THREADS;
+  constexpr int RES_PER = 32 * BN / SK_THREADS, PAIR_PER = 32 * BN / 2 / SK_THREADS;
   float res_in[EPI == EPI_RESID ? RES_PER : 1];
   float rc_in[EPI == EPI_QKV ? PAIR_PER : 1], rs_in[EPI == EPI_QKV ? PAIR_PER : 1];
   if (EPI == EPI_RESID) {
 #pragma unroll
     for (int i = 0; i < RES_PER; ++i) {
-      const int e = tid + i * SK_THREADS, r = m0 + (e >> 6), c = n0 + (e & 63);
+      const int e = tid + i * SK_THREADS, r = m0 + e / BN, c = n0 + e % BN;
       res_in[i] = (r < M && c < N) ? a.resid[(size_t)r * N + c] : 0.f;
     }
   }
@@ -357,7 +363,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
     const int d = a.d, hd = a.hd, half = hd >> 1;
 #pragma unroll
     for (int i = 0; i < PAIR_PER; ++i) {
-      const int e = tid + i * SK_THREADS, r = m0 + (e >> 5), col = n0 + 2 * (e & 31);
+      const int e = tid + i * SK_THREADS, r = m0 + e / (BN / 2), col = n0 + 2 * (e % (BN / 2));
       rc_in[i] = 1.f;
       rs_in[i] = 0.f;
       if (r < M && col < N && col < d + a.kvh * hd) {
@@ -378,15 +384,15 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
 #pragma unroll
   for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[0][j] = dacc[1][j] = 0.0;
 
-  // one chunk [kb, kb + kn) of the 96 staged rows, flat float4 index f = r * (kn/4) + c
-  float4 st[SK_PER_THREAD];
+  // one chunk [kb, kb + kn) of the ROWS staged rows, flat float4 index f = r * (kn/4) + c
+  float4 st[PER_THREAD];
   auto gload = [&](int kb, int kn) {
     const int f4 = kn >> 2;
 #pragma unroll
-    for (int i = 0; i < SK_PER_THREAD; ++i) {
+    for (int i = 0; i < PER_THREAD; ++i) {
       const int f = tid + i * SK_THREADS;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (f < SK_ROWS * f4) {
+      if (f < ROWS * f4) {
         const int r = f / f4, c = f - r * f4;
         if (r < 32) {
           if (m0 + r < M) v = *reinterpret_cast<const float4*>(a.A + (size_t)(m0 + r) * K + kb + 4 * c);
@@ -400,9 +406,9 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   auto sstore = [&](int kn) {
     const int f4 = kn >> 2;
 #pragma unroll
-    for (int i = 0; i < SK_PER_THREAD; ++i) {
+    for (int i = 0; i < PER_THREAD; ++i) {
       const int f = tid + i * SK_THREADS;
-      if (f < SK_ROWS * f4) {
+      if (f < ROWS * f4) {
         const int r = f / f4, c = f - r * f4;
         *reinterpret_cast<float4*>(stg + r * ldsw + 4 * c) = st[i];
       }
@@ -419,15 +425,17 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
     for (int g = w; g < (kn >> 3); g += KW) {
       const float4 av = *reinterpret_cast<const float4*>(stg + row * ldsw + 8 * g + kofs);
       const float4 b0 = *reinterpret_cast<const float4*>(stg + (32 + row) * ldsw + 8 * g + kofs);
-      const float4 b1 = *reinterpret_cast<const float4*>(stg + (64 + row) * ldsw + 8 * g + kofs);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0.x, acc0, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b0.y, acc0, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b0.z, acc0, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b0.w, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1.y, acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b1.z, acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b1.w, acc1, 0, 0, 0);
+      if constexpr (NACC == 2) {
+        const float4 b1 = *reinterpret_cast<const float4*>(stg + (64 + row) * ldsw + 8 * g + kofs);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1.y, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b1.z, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b1.w, acc1, 0, 0, 0);
+      }
     }
     if (CARRY) {   // at most kc / 8 / KW = 5 groups (40 k) per wave per chunk in fp32
 #pragma unroll
@@ -442,21 +450,22 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   __syncthreads();   // the staging area becomes the reduction area
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    red[((w * 2 + 0) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[0][j & (CARRY ? 15 : 0)] : (PT)acc0[j];
-    red[((w * 2 + 1) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[1][j & (CARRY ? 15 : 0)] : (PT)acc1[j];
+    red[((w * NACC + 0) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[0][j & (CARRY ? 15 : 0)] : (PT)acc0[j];
+    if constexpr (NACC == 2)
+      red[((w * 2 + 1) * 16 + j) * 64 + lane] = CARRY ? (PT)dacc[1][j & (CARRY ? 15 : 0)] : (PT)acc1[j];
   }
   __syncthreads();
   // fixed-order sum of the KW partials; with one K slice it is rounded once and
   // kept in slot w = 0, else published for the last slice of the tile
   const int tile_id = blockIdx.y * gridDim.x + blockIdx.x;
-  double* wsp = a.ws + (size_t)tile_id * ks * 2048;
-  for (int e = tid; e < 2 * 16 * 64; e += blockDim.x) {
+  double* wsp = a.ws + (size_t)tile_id * ks * TE;
+  for (int e = tid; e < TE; e += blockDim.x) {
     double s = 0.0;
-    for (int ww = 0; ww < KW; ++ww) s += (double)red[ww * 2 * 16 * 64 + e];
+    for (int ww = 0; ww < KW; ++ww) s += (double)red[ww * TE + e];
     if (ks == 1)
       red[e] = (PT)(float)s;
     else
-      st_dev(wsp + (size_t)blockIdx.z * 2048 + e, s);
+      st_dev(wsp + (size_t)blockIdx.z * TE + e, s);
   }
   if (ks > 1) {
     __shared__ int is_last;
@@ -468,7 +477,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
     __syncthreads();
     if (!is_last) return;
     // the last slice: sum the ks partials of every element in slice order
-    constexpr int EPT = 2048 / SK_THREADS;   // elements per thread
+    constexpr int EPT = TE / SK_THREADS;   // elements per thread
     constexpr int ZB = 16;                  // partials loaded at once
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
@@ -477,7 +486,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
       for (int z0 = 0; z0 < ks; z0 += ZB) {
         double v[ZB];
 #pragma unroll
-        for (int u = 0; u < ZB; ++u) v[u] = z0 + u < ks ? ld_dev(wsp + (size_t)(z0 + u) * 2048 + e) : 0.0;
+        for (int u = 0; u < ZB; ++u) v[u] = z0 + u < ks ? ld_dev(wsp + (size_t)(z0 + u) * TE + e) : 0.0;
 #pragma unroll
         for (int u = 0; u < ZB; ++u) acc += v[u];
       }
@@ -486,7 +495,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
     if (tid == 0) st_dev(a.tickets + tile_id, 0);   // every slice has arrived: re-arm
   }
   __syncthreads();
-  // finished value of local output (rl in 0..31, cl in 0..63)
+  // finished value of local output (rl in 0..31, cl in 0..BN-1)
   auto tile = [&](int rl, int cl) -> float {
     const int t = cl >> 5, ln = (cl & 31) + 32 * ((rl & 7) >> 2), j = 4 * (rl >> 3) + (rl & 3);
     return (float)red[(t * 16 + j) * 64 + ln];
@@ -496,7 +505,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
 #pragma unroll
     for (int i = 0; i < RES_PER; ++i) {
       const int e = tid + i * SK_THREADS;
-      const int rl = e >> 6, cl = e & 63, r = m0 + rl, c = n0 + cl;
+      const int rl = e / BN, cl = e % BN, r = m0 + rl, c = n0 + cl;
       if (r < M && c < N) a.resid[(size_t)r * N + c] = res_in[i] + tile(rl, cl);
     }
   } else if (EPI == EPI_QKV) {
@@ -504,7 +513,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
 #pragma unroll
     for (int i = 0; i < PAIR_PER; ++i) {
       const int e = tid + i * SK_THREADS;
-      const int rl = e >> 5, cl = 2 * (e & 31), r = m0 + rl, col = n0 + cl;
+      const int rl = e / (BN / 2), cl = 2 * (e % (BN / 2)), r = m0 + rl, col = n0 + cl;
       if (r >= M || col >= N) continue;
       float y0 = tile(rl, cl), y1 = tile(rl, cl + 1);
       int c;
@@ -557,6 +566,12 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   }
 }
 
+// narrow split-K tile width of an epilogue: 32 where the epilogue allows it
+template <int EPI>
+constexpr int sk_narrow() {
+  return (EPI == EPI_QKV || EPI == EPI_RESID) ? 32 : 64;
+}
+
 template <int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   if (a.K % BK != 0) return hipErrorInvalidValue;   // whole K steps (and 8-byte bfloat16 loads)
@@ -566,31 +581,44 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   // at 32 rows: measured 49 us against 61 us split-K at 32 x 32000 x 768)
   if (EPI != EPI_CLS && a.M <= 256 && blocks(a.M > 32 ? 64 : 32) < 256) {
     // small problem: split K across the 8 waves of a workgroup, and, when there
-    // are few tiles (<= 64: measured break-even at the 15M b256 shapes), across
-    // workgroups (grid.z) until about 256 workgroups run
-    dim3 grid((a.N + 63) / 64, (a.M + 31) / 32, 1);
+    // are few tiles, across workgroups (grid.z).  Where 64-wide tiles leave CUs
+    // idle, Q/K/V and the residual projections take 32-wide ones (twice the
+    // workgroups, half the MFMA chain and partial tile each: 15M b256 Q/K/V 15.7 ->
+    // 11.6 us, Wo 11.0 -> 8.6; 110M b32 Wo 12.6 -> 9.6, W2 14.6 -> 11.4) and are
+    // split up to 128 tiles towards 512 workgroups; SwiGLU keeps 64-wide tiles (a
+    // W1 and a W3 block per tile), split up to 64 tiles towards 256 workgroups
+    // (measured break-even and best at the 15M b256 and 110M b32 shapes).
+    const int tiles64 = ((a.N + 63) / 64) * ((a.M + 31) / 32);
+    const int bn = (sk_narrow<EPI>() == 32 && tiles64 < 256) ? 32 : 64;
+    const int split_below = bn == 32 ? 128 : 64, target = bn == 32 ? 512 : 256;
+    dim3 grid((a.N + bn - 1) / bn, (a.M + 31) / 32, 1);
     const int tiles = grid.x * grid.y;
+    const size_t tile_bytes = (size_t)(bn / 32) * 1024 * sizeof(double);
     int ks = 1;
-    if (a.ws != nullptr && tiles <= 64) {
+    if (a.ws != nullptr && tiles <= split_below) {
       // slices at least 128 deep once K allows (110M b32: Q/K/V 19.8 -> 15.1 us with 6
       // slices of 128 instead of 8 of 96; 64 and 256 measured worse)
-      ks = std::min(std::min((256 + tiles - 1) / tiles, kSkMaxSlices), std::max(1, a.K / (a.K >= 768 ? 128 : 64)));
-      while (ks > 1 && (size_t)tiles * ks * 2048 * sizeof(double) > kSkWorkspaceBytes) --ks;
+      ks = std::min(std::min((target + tiles - 1) / tiles, kSkMaxSlices), std::max(1, a.K / (a.K >= 768 ? 128 : 64)));
+      while (ks > 1 && (size_t)tiles * ks * tile_bytes > kSkWorkspaceBytes) --ks;
     }
     int kz = (a.K + ks - 1) / ks;
     kz = (kz + 31) / 32 * 32;
     ks = (a.K + kz - 1) / kz;
     grid.z = ks;
     const int kc = kz <= SK_KC ? kz : 256;
-    const size_t shmem = sk_lds_bytes(kc, a.carry);
+    const size_t shmem = sk_lds_bytes(kc, a.carry, bn);
     // the staging area may exceed the default 64 KiB dynamic LDS limit (160 KiB per CU on gfx950)
     static bool lds_raised = false;
     if (!lds_raised) {
-      const int most = (int)std::max(sk_lds_bytes(SK_KC, false), sk_lds_bytes(SK_KC, true));
-      const void* fns[4] = {reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, false>),
-                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, false>),
-                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, true>),
-                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, true>)};
+      const int most = (int)std::max(sk_lds_bytes(SK_KC, false, 64), sk_lds_bytes(SK_KC, true, 64));
+      const void* fns[8] = {reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, false, 64>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, false, 64>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, true, 64>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, true, 64>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, false, sk_narrow<EPI>()>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, false, sk_narrow<EPI>()>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, false, true, sk_narrow<EPI>()>),
+                            reinterpret_cast<const void*>(&k_gemm_sk<EPI, true, true, sk_narrow<EPI>()>)};
       for (const void* fn : fns) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, most);
         if (e != hipSuccess) return e;
@@ -598,16 +626,23 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
       lds_raised = true;
     }
     if (nparts) *nparts = grid.x;
-#define LD_GEMM_SK_LAUNCH(CARRY, BF) \
-  hipExtLaunchKernelGGL((k_gemm_sk<EPI, CARRY, BF>), grid, dim3(SK_THREADS), shmem, s, a.ev_start, \
+#define LD_GEMM_SK_LAUNCH(CARRY, BF, BN) \
+  hipExtLaunchKernelGGL((k_gemm_sk<EPI, CARRY, BF, BN>), grid, dim3(SK_THREADS), shmem, s, a.ev_start, \
                         a.ev_stop, 0, a, kc, kz)
-    if (a.bf16) {
-      if (a.carry) LD_GEMM_SK_LAUNCH(true, true);
-      else LD_GEMM_SK_LAUNCH(false, true);
+#define LD_GEMM_SK_LAUNCH2(BN)                             \
+  if (a.bf16) {                                            \
+    if (a.carry) LD_GEMM_SK_LAUNCH(true, true, BN);        \
+    else LD_GEMM_SK_LAUNCH(false, true, BN);               \
+  } else {                                                 \
+    if (a.carry) LD_GEMM_SK_LAUNCH(true, false, BN);       \
+    else LD_GEMM_SK_LAUNCH(false, false, BN);              \
+  }
+    if (bn == 64) {
+      LD_GEMM_SK_LAUNCH2(64)
     } else {
-      if (a.carry) LD_GEMM_SK_LAUNCH(true, false);
-      else LD_GEMM_SK_LAUNCH(false, false);
+      LD_GEMM_SK_LAUNCH2(sk_narrow<EPI>())
     }
+#undef LD_GEMM_SK_LAUNCH2
 #undef LD_GEMM_SK_LAUNCH
     return hipGetLastError();
   }

@@ -17,6 +17,14 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// The same butterfly within each aligned group of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 __device__ __forceinline__ double wave_max(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));

@@ -103,6 +103,7 @@ void make_layout(const ld_config* c, Layout* L) {
   L->attn_ticket = take((size_t)kMaxAttnParts * 4);
   L->sk_ws = take(kSkWorkspaceBytes);
   L->sk_ticket = take((size_t)kSkMaxTiles * 4);
+  L->ssq = take((size_t)kSsqRows * ((d + 31) / 32) * 8);
   L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
   L->arg_val = take(L->arg_parts * 4);
   L->arg_idx = take(L->arg_parts * 4);
@@ -418,6 +419,27 @@ int layers_gemv(ld_model* m, int pos) {
   return LD_OK;
 }
 
+// Whether a pass over `rows` rows carries the layers' RMSNorms inside the
+// projections: every projection takes the small-problem GEMM, which then
+// receives each row's sums of squares from the kernel that wrote the row (the
+// embedding, Wo and W2 epilogues) and normalises while staging its input, so no
+// norm kernel runs between them.
+bool carried_norm(const ld_model* m, int rows) {
+  const ld_config& c = m->c;
+  const int d = c.dim;
+  return rows > 1 && rows <= kSsqRows && d % 32 == 0 && gemm_small_path(rows, d + 2 * m->kvd) &&
+         gemm_small_path(rows, d) && gemm_small_path(rows, 2 * c.hidden_dim);
+}
+
+// token embeddings of `rows` rows into x (with the sums of squares the first
+// layer's carried norm reads)
+hipError_t embed_rows(ld_model* m, const int* tok, int rows, const int* pos_src, int* pos_dst) {
+  const ld_config& c = m->c;
+  return launch_embed(tok, m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x), rows, c.dim, c.vocab_size,
+                      m->at<int>(m->lay.err), pos_src, pos_dst,
+                      carried_norm(m, rows) ? m->at<double>(m->lay.ssq) : nullptr, m->stream);
+}
+
 // rows = B * n_tok rows (sequence-major) on the MFMA GEMM path.
 int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
   const ld_config& c = m->c;
@@ -428,16 +450,22 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
   float* q = m->at<float>(m->lay.q);
   float* att = m->at<float>(m->lay.att);
   float* g = m->at<float>(m->lay.g);
+  const bool cn = carried_norm(m, rows);
+  double* ssq = cn ? m->at<double>(m->lay.ssq) : nullptr;
   for (int l = 0; l < c.n_layers; ++l) {
-    LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gatt), rows, d, 1, 0, c.norm_eps,
-                                   m->stream));
+    if (!cn)
+      LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gatt), rows, d, 1, 0, c.norm_eps,
+                                     m->stream));
     {
       ProfScope ps(m, K_QKV, true);
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = xn; a.W = m->wlayer(l, m->lay.o_wqkv); a.bf16 = m->bf16; a.M = rows; a.N = d + 2 * m->kvd; a.K = d;
-      a.carry = m->carry; a.kvh = m->kvh;
+      a.A = cn ? x : xn; a.W = m->wlayer(l, m->lay.o_wqkv); a.bf16 = m->bf16; a.M = rows; a.N = d + 2 * m->kvd;
+      a.K = d; a.carry = m->carry; a.kvh = m->kvh;
+      if (cn) {
+        a.norm_gain = m->layer(l, m->lay.o_gatt); a.ssq_in = ssq; a.norm_eps = c.norm_eps;
+      }
       a.q_out = q; a.kc = m->kc(l); a.vc = m->vc(l);
       a.rcos = m->at<float>(m->lay.rope_cos); a.rsin = m->at<float>(m->lay.rope_sin);
       a.pos = pos; a.n_tok = n_tok; a.d = d; a.hd = m->hd; a.H = c.n_heads;
@@ -460,18 +488,22 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = att; a.W = m->wlayer(l, m->lay.o_wo); a.bf16 = m->bf16; a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
-      a.resid = x;
+      a.resid = x; a.ssq_out = ssq;
       LD_TRY_HIP(launch_gemm_resid(a, m->stream));
     }
-    LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gffn), rows, d, 1, 0, c.norm_eps,
-                                   m->stream));
+    if (!cn)
+      LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gffn), rows, d, 1, 0, c.norm_eps,
+                                     m->stream));
     {
       ProfScope ps(m, K_W13, true);
       GemmArgs a{};
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
-      a.A = xn; a.W = m->wlayer(l, m->lay.o_w13); a.bf16 = m->bf16; a.M = rows; a.N = 2 * f; a.K = d; a.carry = m->carry;
-      a.g_out = g; a.f = f;
+      a.A = cn ? x : xn; a.W = m->wlayer(l, m->lay.o_w13); a.bf16 = m->bf16; a.M = rows; a.N = 2 * f; a.K = d;
+      a.carry = m->carry; a.g_out = g; a.f = f;
+      if (cn) {
+        a.norm_gain = m->layer(l, m->lay.o_gffn); a.ssq_in = ssq; a.norm_eps = c.norm_eps;
+      }
       LD_TRY_HIP(launch_gemm_swiglu(a, m->stream));
     }
     {
@@ -480,7 +512,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
       a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = g; a.W = m->wlayer(l, m->lay.o_w2); a.bf16 = m->bf16; a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
-      a.resid = x;
+      a.resid = x; a.ssq_out = l + 1 < c.n_layers ? ssq : nullptr;   // the next layer's Q/K/V norm
       LD_TRY_HIP(launch_gemm_resid(a, m->stream));
     }
   }
@@ -557,7 +589,6 @@ int build_step_graph(ld_model* m, int batch, float* dev_logits) {
     LD_TRY_HIP(hipGraphExecDestroy(m->gexec));
     m->gexec = nullptr;
   }
-  const ld_config& c = m->c;
   hipStream_t user = m->stream;
   m->stream = m->cap_stream;
   m->dev_pos = true;
@@ -567,9 +598,7 @@ int build_step_graph(ld_model* m, int batch, float* dev_logits) {
     rc = LD_E_HIP;
   } else {
     int* pd = m->at<int>(m->lay.pos_dev);
-    if (launch_embed(m->at<int>(m->lay.next), m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x), batch,
-                     c.dim, c.vocab_size, m->at<int>(m->lay.err), pd + 1, pd, m->stream) != hipSuccess)
-      rc = LD_E_HIP;
+    if (embed_rows(m, m->at<int>(m->lay.next), batch, pd + 1, pd) != hipSuccess) rc = LD_E_HIP;
     if (rc == LD_OK) rc = (batch == 1) ? layers_gemv(m, 0) : layers_gemm(m, batch, 1, 0);
     if (rc == LD_OK) rc = head(m, batch, 1, false, dev_logits, 1, 0, nullptr);
     if (hipStreamEndCapture(m->cap_stream, &g) != hipSuccess && rc == LD_OK) rc = LD_E_HIP;
@@ -732,9 +761,7 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
     int rc = enqueue_host_tokens(m, tokens, (size_t)batch, m->at<int>(m->lay.tok));
     if (rc != LD_OK) return rc;
   }
-  const ld_config& c = m->c;
-  LD_TRY_HIP(launch_embed(d_tok, m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x), batch, c.dim,
-                          c.vocab_size, m->at<int>(m->lay.err), nullptr, nullptr, m->stream));
+  LD_TRY_HIP(embed_rows(m, d_tok, batch, nullptr, nullptr));
   int rc = (batch == 1) ? layers_gemv(m, m->pos) : layers_gemm(m, batch, 1, m->pos);
   if (rc != LD_OK) return rc;
   rc = head(m, batch, 1, false, dev_logits, 1, 0, dev_next);
@@ -769,9 +796,7 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
                   sizeof(int32_t) * nc);
     int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows, m->at<int>(m->lay.tok));
     if (rc != LD_OK) return rc;
-    LD_TRY_HIP(launch_embed(m->at<int>(m->lay.tok), m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x),
-                            rows, c.dim, c.vocab_size, m->at<int>(m->lay.err), nullptr, nullptr,
-                            m->stream));
+    LD_TRY_HIP(embed_rows(m, m->at<int>(m->lay.tok), rows, nullptr, nullptr));
     rc = (rows == 1) ? layers_gemv(m, pos0 + t0) : layers_gemm(m, rows, nc, pos0 + t0);
     if (rc != LD_OK) return rc;
     const bool last = t0 + nc >= n_tokens;

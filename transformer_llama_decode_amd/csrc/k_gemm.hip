@@ -384,6 +384,15 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
 #pragma unroll
   for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[0][j] = dacc[1][j] = 0.0;
 
+  // RMSNorm applied while staging A (Q/K/V and SwiGLU when norm_gain is set):
+  // the A slots (the first G_SLOTS of each thread) also fetch the gains of their
+  // columns, and each of the 32 rows' scale comes from its sums of squares
+  constexpr bool CAN_NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU;
+  const bool nrm = CAN_NORM && a.norm_gain != nullptr;
+  constexpr int G_SLOTS = CAN_NORM ? (32 * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS : 1;
+  __shared__ double inv_s[32];
+  float4 gst[G_SLOTS];
+
   // one chunk [kb, kb + kn) of the ROWS staged rows, flat float4 index f = r * (kn/4) + c
   float4 st[PER_THREAD];
   auto gload = [&](int kb, int kn) {
@@ -396,6 +405,8 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
         const int r = f / f4, c = f - r * f4;
         if (r < 32) {
           if (m0 + r < M) v = *reinterpret_cast<const float4*>(a.A + (size_t)(m0 + r) * K + kb + 4 * c);
+          if (CAN_NORM && i < G_SLOTS && nrm)
+            gst[i < G_SLOTS ? i : 0] = *reinterpret_cast<const float4*>(a.norm_gain + kb + 4 * c);
         } else if (n0 + r - 32 < N) {
           v = load_w4<BF>(a.W, (size_t)(n0 + r - 32) * K + kb + 4 * c);
         }
@@ -410,12 +421,40 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
       const int f = tid + i * SK_THREADS;
       if (f < ROWS * f4) {
         const int r = f / f4, c = f - r * f4;
-        *reinterpret_cast<float4*>(stg + r * ldsw + 4 * c) = st[i];
+        float4 v = st[i];
+        if (CAN_NORM && i < G_SLOTS && nrm && r < 32) {
+          const double inv = inv_s[r];
+          const float4 g = gst[i < G_SLOTS ? i : 0];
+          v.x = (float)((double)v.x * inv * (double)g.x);
+          v.y = (float)((double)v.y * inv * (double)g.y);
+          v.z = (float)((double)v.z * inv * (double)g.z);
+          v.w = (float)((double)v.w * inv * (double)g.w);
+        }
+        *reinterpret_cast<float4*>(stg + r * ldsw + 4 * c) = v;
       }
     }
   };
 
   gload(kbeg, min(kc, kend - kbeg));
+  if (nrm && tid < 32) {
+    // 1 / sqrt(mean square + eps) of row m0 + tid, its d / 32 group sums added in order
+    // (the loop's first barrier publishes it before the first staging)
+    const int r = m0 + tid, nps = K / 32;
+    double inv = 0.0;
+    if (r < M) {
+      const double* p = a.ssq_in + (size_t)r * nps;
+      double ss = 0.0;
+      for (int g0 = 0; g0 < nps; g0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = g0 + u < nps ? p[g0 + u] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ss += v[u];
+      }
+      inv = 1.0 / sqrt(ss / (double)K + a.norm_eps);
+    }
+    inv_s[tid] = inv;
+  }
   for (int kb = kbeg; kb < kend; kb += kc) {
     const int kn = min(kc, kend - kb);
     __syncthreads();   // every wave is done reading the previous chunk
@@ -502,11 +541,22 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   };
 
   if (EPI == EPI_RESID) {
+    // with ssq_out, also the sum of squares of each updated row's 32-column group:
+    // the 32 lanes of a half wave hold one row's group (BN and SK_THREADS are
+    // multiples of 32), summed by a fixed butterfly
 #pragma unroll
     for (int i = 0; i < RES_PER; ++i) {
       const int e = tid + i * SK_THREADS;
       const int rl = e / BN, cl = e % BN, r = m0 + rl, c = n0 + cl;
-      if (r < M && c < N) a.resid[(size_t)r * N + c] = res_in[i] + tile(rl, cl);
+      float y = 0.f;
+      if (r < M && c < N) {
+        y = res_in[i] + tile(rl, cl);
+        a.resid[(size_t)r * N + c] = y;
+      }
+      if (a.ssq_out != nullptr) {
+        const double sq = group_sum<32>((double)y * (double)y);
+        if ((lane & 31) == 0 && r < M && c < N) a.ssq_out[(size_t)r * (N / 32) + c / 32] = sq;
+      }
     }
   } else if (EPI == EPI_QKV) {
     const int d = a.d, hd = a.hd;
@@ -572,14 +622,25 @@ constexpr int sk_narrow() {
   return (EPI == EPI_QKV || EPI == EPI_RESID) ? 32 : 64;
 }
 
+// M x N projections with few 64- or 32-row tiles of 128 columns: the split-K kernel
+bool small_problem(int M, int N) {
+  const int nb = (N + 127) / 128, bm = M > 32 ? 64 : 32;
+  return M <= 256 && ((M + bm - 1) / bm) * nb < 256;
+}
+
 template <int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   if (a.K % BK != 0) return hipErrorInvalidValue;   // whole K steps (and 8-byte bfloat16 loads)
+  const bool small = EPI != EPI_CLS && small_problem(a.M, a.N);
+  // the carried RMSNorm exists on the split-K kernel only, for the epilogues that take it
+  if (a.ssq_out != nullptr && (!small || EPI != EPI_RESID || a.N % 32 != 0)) return hipErrorInvalidValue;
+  if (a.norm_gain != nullptr && (!small || (EPI != EPI_QKV && EPI != EPI_SWIGLU) || a.ssq_in == nullptr))
+    return hipErrorInvalidValue;
   const int nb = (a.N + 127) / 128;
   auto blocks = [&](int bm) { return ((a.M + bm - 1) / bm) * nb; };
   // (the classifier, N = vocabulary, has tiles enough for the LDS-tiled kernel even
   // at 32 rows: measured 49 us against 61 us split-K at 32 x 32000 x 768)
-  if (EPI != EPI_CLS && a.M <= 256 && blocks(a.M > 32 ? 64 : 32) < 256) {
+  if (small) {
     // small problem: split K across the 8 waves of a workgroup, and, when there
     // are few tiles, across workgroups (grid.z).  Where 64-wide tiles leave CUs
     // idle, Q/K/V and the residual projections take 32-wide ones (twice the
@@ -693,6 +754,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
 }
 
 }  // namespace
+
+bool gemm_small_path(int M, int N) { return small_problem(M, N); }
 
 hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s) {
   if (a.kvh <= 0 || a.N != a.d + 2 * a.kvh * a.hd) return hipErrorInvalidValue;

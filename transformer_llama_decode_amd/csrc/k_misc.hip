@@ -11,7 +11,7 @@ namespace {
 // id (only possible for ids read from device memory) is replaced by 0 and flagged.
 template <bool BF>
 __global__ void __launch_bounds__(256) k_embed(const int* tok, const void* E, float* x, int d, int V,
-                                               int* err, const int* pos_src, int* pos_dst) {
+                                               int* err, const int* pos_src, int* pos_dst, double* ssq) {
   const int r = blockIdx.x;
   if (pos_dst != nullptr && r == 0 && threadIdx.x == 0) *pos_dst = *pos_src;
   int t = tok[r];
@@ -20,12 +20,35 @@ __global__ void __launch_bounds__(256) k_embed(const int* tok, const void* E, fl
     t = 0;
   }
   float4* dst = reinterpret_cast<float4*>(x + (size_t)r * d);
+  const int d4 = d >> 2;
+  if (ssq != nullptr) {
+    // the row's sums of squares per 32-column group (8 consecutive lanes), for the
+    // first layer's RMSNorm carried by the Q/K/V GEMM; every lane takes every pass
+    for (int j0 = 0; j0 < d4; j0 += 256) {
+      const int j = j0 + (int)threadIdx.x;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < d4) {
+        if (BF)
+          v = bf16x4(reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(E) + (size_t)t * d)[j]);
+        else
+          v = reinterpret_cast<const float4*>(static_cast<const float*>(E) + (size_t)t * d)[j];
+        dst[j] = v;
+      }
+      double sq = (double)v.x * (double)v.x;
+      sq = fma((double)v.y, (double)v.y, sq);
+      sq = fma((double)v.z, (double)v.z, sq);
+      sq = fma((double)v.w, (double)v.w, sq);
+      sq = group_sum<8>(sq);
+      if ((threadIdx.x & 7) == 0 && j < d4) ssq[(size_t)r * (d >> 5) + (j >> 3)] = sq;
+    }
+    return;
+  }
   if (BF) {
     const uint2* src = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(E) + (size_t)t * d);
-    for (int j = threadIdx.x; j < (d >> 2); j += 256) dst[j] = bf16x4(src[j]);
+    for (int j = threadIdx.x; j < d4; j += 256) dst[j] = bf16x4(src[j]);
   } else {
     const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(E) + (size_t)t * d);
-    for (int j = threadIdx.x; j < (d >> 2); j += 256) dst[j] = src[j];
+    for (int j = threadIdx.x; j < d4; j += 256) dst[j] = src[j];
   }
 }
 
@@ -119,11 +142,14 @@ __global__ void k_set_int(int* p, int v) {
 }  // namespace
 
 hipError_t launch_embed(const int* tok, const void* E, bool bf16, float* x, int rows, int d, int V,
-                        int* err, const int* pos_src, int* pos_dst, hipStream_t s) {
+                        int* err, const int* pos_src, int* pos_dst, double* ssq, hipStream_t s) {
+  if (ssq != nullptr && d % 32 != 0) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(k_embed<true>, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst);
+    hipLaunchKernelGGL(k_embed<true>, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst,
+                       ssq);
   else
-    hipLaunchKernelGGL(k_embed<false>, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst);
+    hipLaunchKernelGGL(k_embed<false>, dim3(rows), dim3(256), 0, s, tok, E, x, d, V, err, pos_src, pos_dst,
+                       ssq);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS =
 struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
-  size_t x, xn, q, att, g, attn_part, attn_ticket, sk_ws, sk_ticket, arg_val, arg_idx, tok, next, err;
+  size_t x, xn, q, att, g, attn_part, attn_ticket, sk_ws, sk_ticket, ssq, arg_val, arg_idx, tok, next, err;
   size_t csum;         // one 64-bit accumulator of ld_weights_checksum
   size_t pos_dev, gen;
   size_t total;
@@ -139,7 +139,20 @@ struct GemmArgs {
   double* ws;
   int* tickets;
   int tiles_n, tiles_m;   // LDS-tiled kernel: output tiles along N and M (set by its launcher)
+  // RMSNorm carried by the small-problem GEMMs instead of a kernel of its own
+  // (rows of K = d columns; sums of squares kept per 32-column group, [M][d/32]):
+  //  * ssq_out (residual epilogue): the sums of squares of the updated rows;
+  //  * norm_gain (Q/K/V, SwiGLU): A holds raw rows whose sums are in ssq_in; each
+  //    element is staged as (float)(a * (1 / sqrt(sum / d + eps)) * gain[k]).
+  double* ssq_out;
+  const double* ssq_in;
+  const float* norm_gain;
+  double norm_eps;
 };
+// true when an M x N projection runs on the small-problem (split-K) GEMM, the
+// only one that takes ssq_out / norm_gain
+bool gemm_small_path(int M, int N);
+constexpr int kSsqRows = 256;   // rows the small-problem GEMM takes at most
 // capacity of the split-K workspace: tiles that may be split, slices per tile, bytes
 constexpr int kSkMaxTiles = 256;
 constexpr int kSkMaxSlices = 16;
@@ -149,9 +162,10 @@ hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_cls(const GemmArgs& a, int* nparts, hipStream_t s);
 
-// pos_dst/pos_src (both or neither): the first workgroup also copies *pos_src to *pos_dst
+// pos_dst/pos_src (both or neither): the first workgroup also copies *pos_src to *pos_dst.
+// ssq (may be nullptr): sums of squares of each row's 32-column groups, [rows][d/32].
 hipError_t launch_embed(const int* tok, const void* E, bool bf16, float* x, int rows, int d, int V,
-                        int* err, const int* pos_src, int* pos_dst, hipStream_t s);
+                        int* err, const int* pos_src, int* pos_dst, double* ssq, hipStream_t s);
 // out row i <- rmsnorm(in row i * in_stride + in_offset)
 hipError_t launch_rmsnorm_rows(const float* in, float* out, const float* gain, int rows, int d,
                                int in_stride, int in_offset, double eps, hipStream_t s);

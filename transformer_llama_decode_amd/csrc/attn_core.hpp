@@ -1,5 +1,5 @@
 // attn_core.hpp -- one workgroup's share of causal attention over the KV cache
-// (shared by the attention kernel and the fused attention + output projection).
+// (the decode unit, and below it the prompt-rows unit).
 //
 // A workgroup of 4 waves takes one (row, head, chunk) unit: chunk c of nchunk
 // owns the row's 64-position tiles c, c + nchunk, c + 2 nchunk, ... (online
@@ -7,7 +7,8 @@
 // issue every load of the tile at once -- wave w fetches head dimensions
 // [w*hd/4, (w+1)*hd/4) of the tile's 64 keys (K tiles are [hd/4][64][4], so each
 // load is a float4 per lane, 1 KiB per wave) and the 16 value rows of positions
-// [16w, 16w+16) -- so a tile costs about one HBM round trip.  Then:
+// [16w, 16w+16) -- so a tile costs about one HBM round trip, and up to head dim
+// 128 the chunk's next tile is already in flight while this one is used.  Then:
 //  * scores: each wave's partial dot products over its dimensions meet in LDS
 //    and are summed in a fixed order (lane j = position j of the tile);
 //  * online softmax per wave with wave-level max/sum butterflies: every wave
@@ -132,8 +133,15 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.0;
 
+  // up to head dim 128 the next tile of the chunk is loaded into a second register
+  // set while this one is used (two tiles in flight per workgroup); wider heads
+  // would spill, so they load it after
+  constexpr bool kPrefetch = HD <= 128;
+  TileRegs<HD> nxt;
   for (int tile = c; tile < ntiles; tile += nchunk) {
     const int j0 = tile * kTile;
+    if constexpr (kPrefetch)
+      if (tile + nchunk < ntiles) load_tile<HD>(nxt, kt, vb, tile + nchunk, w, lane);
     mask_tile<HD>(cur, tile, kvlen, w);
     // ---- partial scores over this wave's dimensions (4 independent chains)
     double s4[4] = {0.0, 0.0, 0.0, 0.0};
@@ -174,7 +182,10 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
     for (int k = 0; k < DPL; ++k) o[k] = oo[k][0] + oo[k][1];
     m_run = m_new;
     if (tile + nchunk < ntiles) {
-      load_tile<HD>(cur, kt, vb, tile + nchunk, w, lane);
+      if constexpr (kPrefetch)
+        cur = nxt;
+      else
+        load_tile<HD>(cur, kt, vb, tile + nchunk, w, lane);
       __syncthreads();   // sp / es are rewritten by the next tile
     }
   }

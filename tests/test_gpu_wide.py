@@ -4,7 +4,7 @@ Two layers of the 7B shape (4096 wide, 32 heads of 128, 11008 hidden, 32000
 vocabulary, untied classifier) run the same launches the 7B decode and prefill
 time: the Q/K/V GEMV [12288 x 4096], W1/W3 [22016 x 4096], W2 [4096 x 11008],
 the classifier [32000 x 4096], the split-K MFMA GEMMs with fp64 carries and the
-matrix-core prompt attention at head dim 128.  Every logit of a 40-token prompt
+fp64 prompt attention that wide models keep (head dim 128).  Every logit of a 40-token prompt
 and of 4 decode steps after it is compared with the oracle, for fp32 weights
 with multi-head attention and for bfloat16 weights with 8 key/value heads, and
 one layer run past max_seq over a wrapped ring.  A 2048-wide layer run as a
@@ -81,8 +81,8 @@ WIDE_WINDOW = replace(WIDE, n_layers=1, max_seq=64, max_pos=160)   # ring of 128
 
 
 def test_seven_b_shapes_past_max_seq_every_logit(dev):
-    """the window at head dim 128: a 100-token prompt crosses max_seq (matrix-core prompt
-    attention with window masks), 50 decode steps run past the 128-slot ring's wrap"""
+    """the window at head dim 128: a 100-token prompt crosses max_seq (prompt attention
+    with window masks), 50 decode steps run past the 128-slot ring's wrap"""
     from transformer_llama_decode_amd.model import LlamaDecoder
     cfg, seed = WIDE_WINDOW, 83
     _say("7B-shape layer past max_seq", cfg)

@@ -658,8 +658,8 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
   m->stream = reinterpret_cast<hipStream_t>(hip_stream);
   m->arena = reinterpret_cast<char*>(dev_arena);
   m->pos = 0;
-  // fp32 MFMA sums are carried into fp64 for wide models (K >= 2048)
-  m->carry = cfg->dim >= 2048;
+  // fp32 MFMA sums are carried into fp64 for wide models
+  m->carry = cfg->dim >= kWideDim;
   m->bf16 = cfg->weight_bf16 == 1;
   m->wes = m->bf16 ? 2 : 4;
   {

@@ -25,8 +25,9 @@
 //    contiguous load.  Value rows past the history are read as 0.
 //  * the rescaling of O by exp(m_old - m_new) is one scalar per lane.
 // Scores are fp32 matrix-core sums of fp32 products (relative error ~1e-7 of
-// |q||k|) and O accumulates in fp32; the decode path keeps fp64 sums.  Both are
-// well inside the logits' 1e-4 tolerance (long-prompt parity tests).
+// |q||k|) and O accumulates (and is rescaled) in fp32; the decode path keeps
+// fp64 sums.  Below the wide-model width this stays inside the logits' tolerance
+// (long-prompt parity tests); wide models take the fp64 vector path.
 #include <algorithm>
 
 #include "dev_common.hpp"
@@ -222,8 +223,11 @@ __global__ void __launch_bounds__(64 * NW) k_attn_mfma(AttnArgs a, int qtiles) {
 }  // namespace
 
 bool attention_prefill_supported(const AttnArgs& a) {
-  // (head dim 256 would keep 128 fp32 Q^T and 128 O^T registers per lane and spill)
-  return a.n_tok >= kQRows && a.hd % 32 == 0 && a.hd <= 224 && a.seq_pad % kKeys == 0;
+  // (head dim 256 would keep 128 fp32 Q^T and 128 O^T registers per lane and spill;
+  // wide models keep fp64 sums: at the 7B shape the fp32 scores and O of this
+  // kernel put the 512-token prompt's last logits at 2.2x the tolerance, the fp64
+  // vector path at 0.9x)
+  return a.d < kWideDim && a.n_tok >= kQRows && a.hd % 32 == 0 && a.hd <= 224 && a.seq_pad % kKeys == 0;
 }
 
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t s) {

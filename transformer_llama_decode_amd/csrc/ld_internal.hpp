@@ -88,6 +88,11 @@ hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s);
 // returns the number of arg-max partials written in *nparts
 hipError_t launch_gemv_cls(const GemvArgs& a, int* nparts, hipStream_t s);
 
+// Model width from which fp32 matrix-core sums no longer keep the logits within
+// tolerance on their own: the GEMMs carry their sums into fp64 every 32 k, and
+// prompt attention stays on the fp64 vector path.
+constexpr int kWideDim = 2048;
+
 struct AttnArgs {
   const float* q;      // [rows][d], rotated
   const float* kc;     // K cache of this layer, sequence 0

@@ -9,7 +9,8 @@ and of 4 decode steps after it is compared with the oracle, for fp32 weights
 with multi-head attention and for bfloat16 weights with 8 key/value heads, and
 one layer run past max_seq over a wrapped ring.  A 2048-wide layer run as a
 batch of sequences takes the small-problem GEMM with 32-wide tiles, K split
-over workgroups and fp64 carries.
+over workgroups and fp64 carries; the same layer under a 520-token prompt takes
+the LDS-tiled GEMM with fp64 carries.
 """
 import sys
 from dataclasses import replace
@@ -154,4 +155,33 @@ def test_batched_split_k_with_carries_every_logit(dev, cfg, seed):
             assert r >= 0
             assert_logits(dec[i][b], ref, "seq %d decode pos %d" % (b, P + i))
             assert_token(int(feed[i + 1][b]), ref, "seq %d decode pos %d" % (b, P + i))
+    om.close()
+
+
+# 2048 wide, a 520-token prompt: more than 256 rows, so every projection takes the
+# LDS-tiled MFMA GEMM with fp64 carries (128-row tiles and a ragged 8-row tail), and
+# prompt attention the fp64 vector path that wide models keep
+MID_PROMPT = ModelConfig(dim=2048, n_layers=1, n_heads=16, hidden_dim=5632, vocab_size=4096, max_seq=576,
+                         tied=False)
+
+
+@pytest.mark.parametrize("cfg,seed", [(MID_PROMPT, 86), (replace(MID_PROMPT, weight_bf16=True, n_kv_heads=4), 87)])
+def test_wide_long_prompt_tiled_gemm_every_logit(dev, cfg, seed):
+    from transformer_llama_decode_amd.model import LlamaDecoder
+    _say("2048-wide 520-token prompt", cfg)
+    P = 520
+    gm = LlamaDecoder(cfg, seed)
+    prompt = O.synth_prompt(seed, 0, P, 3, cfg.vocab_size)
+    allp = torch.empty((1, P, cfg.vocab_size), dtype=torch.float32, device=dev)
+    nxt = gm.prefill(prompt[None, :], logits=allp, all_pos=True)
+    allp = allp.cpu().numpy()[0]
+    first = int(nxt.cpu()[0])
+    gm.close()
+    om = O.OracleModel(cfg, seed, nthreads=16)
+    st = om.new_state()
+    for p in range(P):
+        r, ref = om.forward(st, int(prompt[p]), p)
+        assert r >= 0
+        assert_logits(allp[p], ref, "prefill pos %d" % p)
+    assert_token(first, ref, "prefill next")
     om.close()

@@ -104,7 +104,7 @@ void make_layout(const ld_config* c, Layout* L) {
   L->sk_ws = take(kSkWorkspaceBytes);
   L->sk_ticket = take((size_t)kSkMaxTiles * 4);
   L->ssq = take((size_t)kSsqRows * ((d + 31) / 32) * 8);
-  L->arg_parts = std::max((size_t)1024, R * 2 * ((V + 127) / 128));
+  L->arg_parts = std::max((size_t)1024, R * 4 * ((V + 127) / 128));   // up to 4 per 128 columns
   L->arg_val = take(L->arg_parts * 4);
   L->arg_idx = take(L->arg_parts * 4);
   L->tok = take(R * 4);
@@ -534,7 +534,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
   int* next_int = m->at<int>(m->lay.next);
   const int cls_rows = all_pos ? B * n_tok : B;
   int nparts = 0;
-  // capacity of the partial arrays (R rows x the GEMM's 2 partials per 128 columns)
+  // capacity of the partial arrays (R rows x the GEMM's 2 or 4 partials per 128 columns)
   if (cls_rows > m->lay.rows) return LD_E_ARENA;
   if (cls_rows == 1) {
     ProfScope ps(m, K_CLS, true);

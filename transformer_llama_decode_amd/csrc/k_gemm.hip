@@ -33,8 +33,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_CLS = 3 };
 
-constexpr int BK = 32;
-constexpr int LDS_STRIDE = BK + 4;
+constexpr int BK = 32;   // K step of the tiled kernel (64 for the few-row classifier)
 
 // Four consecutive elements idx .. idx+3 (idx a multiple of 4) of a weight
 // matrix held in fp32, or in bfloat16 (an 8-byte load, widened exactly).
@@ -44,21 +43,22 @@ __device__ __forceinline__ float4 load_w4(const void* W, size_t idx) {
   return *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
 }
 
-// Global -> register loads of one K step: BM x 32 values of A, BN x 32 of W;
-// rows past M / N read as zero.  fp32: 8 16-byte loads per row, slot i holds
-// k 4c..4c+3.  bfloat16 (BF): 4 16-byte loads of 8 weights per row, widened
-// into slots 2i and 2i+1 (k 8c..8c+7), so a row is still 64 contiguous bytes
-// per 4 lanes rather than 8-byte pieces.
-template <int ROWS, int NTHR, bool BF, int L>
+// Global -> register loads of one K step: BM x KS values of A, BN x KS of W;
+// rows past M / N read as zero.  fp32: KS/4 16-byte loads per row, slot i holds
+// k 4c..4c+3.  bfloat16 (BF): KS/8 16-byte loads of 8 weights per row, widened
+// into slots 2i and 2i+1 (k 8c..8c+7), so a row is still 2*KS contiguous bytes
+// rather than 8-byte pieces.
+template <int ROWS, int NTHR, bool BF, int L, int KS>
 __device__ __forceinline__ void tile_gload(float4 (&r)[L], const void* __restrict__ src, int row0,
                                            int nrows, int K, int k0, int tid) {
+  constexpr int F4 = KS / 4, U8 = KS / 8;   // 16-byte loads per row: fp32, bfloat16
   if constexpr (BF) {
     static_assert(L % 2 == 0, "two widened slots per bfloat16 load");
 #pragma unroll
     for (int i = 0; i < L / 2; ++i) {
       const int idx = tid + i * NTHR;
-      const int row = idx >> 2, c8 = idx & 3, g = row0 + row;
-      if (idx < ROWS * 4 && g < nrows) {
+      const int row = idx / U8, c8 = idx % U8, g = row0 + row;
+      if (idx < ROWS * U8 && g < nrows) {
         const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)g * K +
                                                         k0 + c8 * 8);
         r[2 * i] = bf16x4(make_uint2(u.x, u.y));
@@ -72,8 +72,8 @@ __device__ __forceinline__ void tile_gload(float4 (&r)[L], const void* __restric
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int idx = tid + i * NTHR;
-      const int row = idx >> 3, c4 = idx & 7, g = row0 + row;
-      if (idx < ROWS * 8 && g < nrows)
+      const int row = idx / F4, c4 = idx % F4, g = row0 + row;
+      if (idx < ROWS * F4 && g < nrows)
         r[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + (size_t)g * K + k0 + c4 * 4);
       else
         r[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -81,14 +81,21 @@ __device__ __forceinline__ void tile_gload(float4 (&r)[L], const void* __restric
   }
 }
 
-template <int ROWS, int NTHR, bool BF, int L>
+// LDS tile rows of a K step: KS values and a 16-byte skew
+template <int KS>
+constexpr int lds_stride() {
+  return KS + 4;
+}
+
+template <int ROWS, int NTHR, bool BF, int L, int KS>
 __device__ __forceinline__ void tile_sstore(const float4 (&r)[L], float* dst, int tid) {
+  constexpr int F4 = KS / 4, U8 = KS / 8, LS = lds_stride<KS>();
   if constexpr (BF) {
 #pragma unroll
     for (int i = 0; i < L / 2; ++i) {
       const int idx = tid + i * NTHR;
-      if (idx < ROWS * 4) {
-        float* p = &dst[(idx >> 2) * LDS_STRIDE + (idx & 3) * 8];
+      if (idx < ROWS * U8) {
+        float* p = &dst[(idx / U8) * LS + (idx % U8) * 8];
         *reinterpret_cast<float4*>(p) = r[2 * i];
         *reinterpret_cast<float4*>(p + 4) = r[2 * i + 1];
       }
@@ -97,19 +104,21 @@ __device__ __forceinline__ void tile_sstore(const float4 (&r)[L], float* dst, in
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int idx = tid + i * NTHR;
-      if (idx < ROWS * 8) *reinterpret_cast<float4*>(&dst[(idx >> 3) * LDS_STRIDE + (idx & 7) * 4]) = r[i];
+      if (idx < ROWS * F4) *reinterpret_cast<float4*>(&dst[(idx / F4) * LS + (idx % F4) * 4]) = r[i];
     }
   }
 }
 
-template <int WM, int WN, int MT, int NT, int EPI, bool CARRY, bool BF>
+template <int WM, int WN, int MT, int NT, int EPI, bool CARRY, bool BF, int KS>
 __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int BM = 32 * MT * WM, BN = 32 * NT * WN;
-  constexpr int AL = (BM * 8 + NTHR - 1) / NTHR;
-  constexpr int BL = (BN * 8 + NTHR - 1) / NTHR;
-  __shared__ float As[2][BM * LDS_STRIDE];
-  __shared__ float Bs[2][BN * LDS_STRIDE];
+  constexpr int LS = lds_stride<KS>();
+  constexpr int AL = (BM * (KS / 4) + NTHR - 1) / NTHR;
+  constexpr int BL = (BN * (KS / 4) + NTHR - 1) / NTHR;
+  static_assert(!CARRY || KS == 32, "fp64 carries every 32 k");
+  __shared__ float As[2][BM * LS];
+  __shared__ float Bs[2][BN * LS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -139,31 +148,31 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
       for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[mt][nt][j] = 0.0;
     }
 
-  tile_gload<BM, NTHR, false>(ra, a.A, m0, M, K, 0, tid);
-  tile_gload<BN, NTHR, BF>(rb, a.W, n0, N, K, 0, tid);
-  tile_sstore<BM, NTHR, false>(ra, As[0], tid);
-  tile_sstore<BN, NTHR, BF>(rb, Bs[0], tid);
+  tile_gload<BM, NTHR, false, AL, KS>(ra, a.A, m0, M, K, 0, tid);
+  tile_gload<BN, NTHR, BF, BL, KS>(rb, a.W, n0, N, K, 0, tid);
+  tile_sstore<BM, NTHR, false, AL, KS>(ra, As[0], tid);
+  tile_sstore<BN, NTHR, BF, BL, KS>(rb, Bs[0], tid);
   __syncthreads();
   int cur = 0;
   const int arow = wm * MT * 32 + (lane & 31), brow = wn * NT * 32 + (lane & 31);
   const int kofs = 4 * (lane >> 5);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool more = k0 + BK < K;
+  for (int k0 = 0; k0 < K; k0 += KS) {
+    const bool more = k0 + KS < K;
     if (more) {
-      tile_gload<BM, NTHR, false>(ra, a.A, m0, M, K, k0 + BK, tid);
-      tile_gload<BN, NTHR, BF>(rb, a.W, n0, N, K, k0 + BK, tid);
+      tile_gload<BM, NTHR, false, AL, KS>(ra, a.A, m0, M, K, k0 + KS, tid);
+      tile_gload<BN, NTHR, BF, BL, KS>(rb, a.W, n0, N, K, k0 + KS, tid);
     }
     const float* as = As[cur];
     const float* bs = Bs[cur];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 8) {
+    for (int kk = 0; kk < KS; kk += 8) {
       float4 av[MT], bv[NT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        av[mt] = *reinterpret_cast<const float4*>(as + (arow + mt * 32) * LDS_STRIDE + kk + kofs);
+        av[mt] = *reinterpret_cast<const float4*>(as + (arow + mt * 32) * LS + kk + kofs);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bv[nt] = *reinterpret_cast<const float4*>(bs + (brow + nt * 32) * LDS_STRIDE + kk + kofs);
+        bv[nt] = *reinterpret_cast<const float4*>(bs + (brow + nt * 32) * LS + kk + kofs);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -186,8 +195,8 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           }
     }
     if (more) {
-      tile_sstore<BM, NTHR, false>(ra, As[cur ^ 1], tid);
-      tile_sstore<BN, NTHR, BF>(rb, Bs[cur ^ 1], tid);
+      tile_sstore<BM, NTHR, false, AL, KS>(ra, As[cur ^ 1], tid);
+      tile_sstore<BN, NTHR, BF, BL, KS>(rb, Bs[cur ^ 1], tid);
     }
     __syncthreads();
     cur ^= 1;
@@ -722,9 +731,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
   g.tiles_n = nb;
   g.tiles_m = (a.M + bm - 1) / bm;
   dim3 grid(((g.tiles_n * g.tiles_m + 7) / 8) * 8);
-  if (nparts) *nparts = nb * 2;
-#define LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, CARRY, BF)                                            \
-  hipExtLaunchKernelGGL((k_gemm<WM, WN, MT, NT, EPI, CARRY, BF>), grid, dim3(THR), 0, s, a.ev_start, \
+  // arg-max partials: one per wave column of a 128-column tile
+  const bool few_rows_cls = bm == 32 && EPI == EPI_CLS && !a.carry && a.K % 64 == 0;
+  if (nparts) *nparts = nb * (few_rows_cls ? 4 : 2);
+#define LD_GEMM_LAUNCH1(WM, WN, MT, NT, THR, CARRY, BF)                                                \
+  hipExtLaunchKernelGGL((k_gemm<WM, WN, MT, NT, EPI, CARRY, BF, BK>), grid, dim3(THR), 0, s, a.ev_start, \
                         a.ev_stop, 0, g)
 #define LD_GEMM_LAUNCH(WM, WN, MT, NT, THR)                                      \
   if (a.bf16) {                                                                  \
@@ -744,6 +755,18 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
       LD_GEMM_LAUNCH(2, 4, 1, 1, 512)
     } else {
       LD_GEMM_LAUNCH(2, 2, 1, 2, 256)
+    }
+  } else if (few_rows_cls) {
+    // the classifier of at most 32 rows: one workgroup per CU, so 4 waves of 32 x 32
+    // keep all four SIMDs' matrix cores busy (2 waves of 32 x 64 leave two idle),
+    // with 64-deep K steps (half the barriers)
+    if constexpr (EPI == EPI_CLS) {
+      if (a.bf16)
+        hipExtLaunchKernelGGL((k_gemm<1, 4, 1, 1, EPI, false, true, 64>), grid, dim3(256), 0, s, a.ev_start,
+                              a.ev_stop, 0, g);
+      else
+        hipExtLaunchKernelGGL((k_gemm<1, 4, 1, 1, EPI, false, false, 64>), grid, dim3(256), 0, s, a.ev_start,
+                              a.ev_stop, 0, g);
     }
   } else {
     LD_GEMM_LAUNCH(1, 2, 1, 2, 128)

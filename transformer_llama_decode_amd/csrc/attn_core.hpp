@@ -23,6 +23,8 @@
 // query sees it (causality, and the sliding window past max_seq) is KvRing's.
 #pragma once
 
+#include <climits>
+
 #include "dev_common.hpp"
 #include "ld_internal.hpp"
 
@@ -43,27 +45,30 @@ struct TileRegs {
   float v[16][DPL];
 };
 
-// Loads the whole tile (every tile index below Sp/64 lies inside the cache);
-// rows past the history are zeroed afterwards by mask_tile.
+// Loads the whole tile (every tile index below Sp/64 lies inside the cache), but
+// slots at or past kvlen re-read the last slot below it, so their cache lines are
+// never fetched; those slots are masked out of the scores and zeroed by mask_tile.
 template <int HD>
 __device__ __forceinline__ void load_tile(TileRegs<HD>& t, const float4* kt, const float* vb, int tile,
-                                          int w, int lane) {
+                                          int w, int lane, int kvlen) {
   constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
   const int j0 = tile * kTile;
-  const float4* kp = kt + ((size_t)tile * (HD / 4) + w * KQ) * kTile + lane;
+  const int last = max(kvlen - 1 - j0, 0);   // last slot of the tile inside the history
+  const float4* kp = kt + ((size_t)tile * (HD / 4) + w * KQ) * kTile + min(lane, last);
 #pragma unroll
   for (int i = 0; i < KQ; ++i) t.k[i] = kp[i * kTile];
-  const float* vp = vb + (size_t)(j0 + 16 * w) * HD + lane * DPL;
+  const float* vp = vb + (size_t)j0 * HD + lane * DPL;
   if (lane * DPL < HD) {
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
+      const float* row = vp + (size_t)min(16 * w + jj, last) * HD;
       if (DPL == 2) {
-        const float2 v2 = *reinterpret_cast<const float2*>(vp + jj * HD);
+        const float2 v2 = *reinterpret_cast<const float2*>(row);
         t.v[jj][0] = v2.x;
         t.v[jj][DPL - 1] = v2.y;
       } else {
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) t.v[jj][k] = vp[jj * HD + k];
+        for (int k = 0; k < DPL; ++k) t.v[jj][k] = row[k];
       }
     }
   } else {
@@ -113,7 +118,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   // speculative first tile (c < nchunk <= Sp/64: inside the cache); unused if
   // the history turns out shorter than c + 1 tiles
   const bool spec = a.pos_dev != nullptr;
-  if (spec) load_tile<HD>(cur, kt, vb, c, w, lane);
+  if (spec) load_tile<HD>(cur, kt, vb, c, w, lane, INT_MAX);
   // the query does not depend on the position either: its load goes out first
   const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)r * a.d + (size_t)h * HD);
   const bool q_lane = threadIdx.x < HD / 4;   // HD / 4 <= 64 < kThreads
@@ -124,7 +129,10 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   const int lo_q = kr.lo(q);
   const int kvlen = min(q + 1, kr.nslots);                  // slots to visit
   const int ntiles = (kvlen + kTile - 1) / kTile;
-  if (!spec && c < ntiles) load_tile<HD>(cur, kt, vb, c, w, lane);   // first tile in flight
+  // a unit that walks the whole history (batched decode) skips the slots past it;
+  // split heads (batch 1) keep plain loads, which measured a little faster there
+  const int fetch_len = nchunk == 1 ? kvlen : INT_MAX;
+  if (!spec && c < ntiles) load_tile<HD>(cur, kt, vb, c, w, lane, fetch_len);   // first tile in flight
   if (q_lane) qs4[threadIdx.x] = qv_in;
   __syncthreads();
 
@@ -141,7 +149,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   for (int tile = c; tile < ntiles; tile += nchunk) {
     const int j0 = tile * kTile;
     if constexpr (kPrefetch)
-      if (tile + nchunk < ntiles) load_tile<HD>(nxt, kt, vb, tile + nchunk, w, lane);
+      if (tile + nchunk < ntiles) load_tile<HD>(nxt, kt, vb, tile + nchunk, w, lane, fetch_len);
     mask_tile<HD>(cur, tile, kvlen, w);
     // ---- partial scores over this wave's dimensions (4 independent chains)
     double s4[4] = {0.0, 0.0, 0.0, 0.0};
@@ -185,7 +193,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
       if constexpr (kPrefetch)
         cur = nxt;
       else
-        load_tile<HD>(cur, kt, vb, tile + nchunk, w, lane);
+        load_tile<HD>(cur, kt, vb, tile + nchunk, w, lane, fetch_len);
       __syncthreads();   // sp / es are rewritten by the next tile
     }
   }
@@ -232,7 +240,7 @@ __device__ __forceinline__ void attn_rows(const AttnArgs a, int h, int b, int t0
   const int ntiles = (kvlen_max + kTile - 1) / kTile;
 
   TileRegs<HD> cur;
-  load_tile<HD>(cur, kt, vb, 0, w, lane);
+  load_tile<HD>(cur, kt, vb, 0, w, lane, INT_MAX);
   for (int i = threadIdx.x; i < R * (HD / 4); i += kThreads) {
     const int rr = i / (HD / 4), c4 = i - rr * (HD / 4);
     qs4[rr][c4] = rr < nrows ? reinterpret_cast<const float4*>(
@@ -293,7 +301,7 @@ __device__ __forceinline__ void attn_rows(const AttnArgs a, int h, int b, int t0
       for (int k = 0; k < DPL; ++k) o[rr][k] = oo[k][0] + oo[k][1];
       m_run[rr] = m_new;
     }
-    if (tile + 1 < ntiles) load_tile<HD>(cur, kt, vb, tile + 1, w, lane);
+    if (tile + 1 < ntiles) load_tile<HD>(cur, kt, vb, tile + 1, w, lane, INT_MAX);
   }
 
 #pragma unroll

@@ -3,9 +3,10 @@
 //
 // Here the projections are dense GEMMs (M = batch or batch x prompt positions),
 // so they run on the CDNA4 matrix cores with v_mfma_f32_32x32x2_f32:
-//  * workgroup tile BM x BN (BN = 128), K step 32, both operands staged in LDS
-//    (row stride 36 floats to spread banks), double buffered with one barrier
-//    per K step; the next tile's global loads are issued before the MFMAs;
+//  * workgroup tile BM x BN (BN = 128), K step 32 (64 for the classifier of at
+//    most 32 rows), both operands staged in LDS (rows skewed by 16 bytes to
+//    spread banks), double buffered with one barrier per K step; the next
+//    tile's global loads are issued before the MFMAs;
 //  * each wave owns (32*MT) x (32*NT) of the tile; a lane reads 4 consecutive k
 //    of its A row and of its W row as one float4, and 4 MFMAs consume them.
 //    Each MFMA sums over 2 k (one per lane half); the k order inside a K step is
@@ -19,6 +20,7 @@
 //    in adjacent lanes), residual add for Wo and W2, the SwiGLU gate for W1/W3
 //    (interleaved 32-row blocks put h1 and h3 of one column in the same lane),
 //    and per-row arg-max partials for the classifier.
+// Small problems (batched decode) take the split-K kernel further below.
 #include <algorithm>
 #include <cmath>
 

@@ -131,3 +131,8 @@ def test_golden_C4_batch32():
 @pytest.mark.timeout(900)
 def test_golden_C5():
     _run("C5")
+
+
+@pytest.mark.timeout(900)
+def test_golden_C5_bfloat16():
+    _run("C5bf16")

@@ -9,6 +9,7 @@ Those greedy sequences are the teacher-forcing inputs of the GPU parity tests.
     python tests/golden/make_golden.py C2 C3 ...     (default: all but C5)
     python tests/golden/make_golden.py C5            (~1.5 h, ~30 GB of RAM)
     python tests/golden/make_golden.py C5bf16        (the same with bfloat16 weights)
+    python tests/golden/make_golden.py C5w           (past max_seq: ~2.5 h)
 """
 import hashlib
 import os
@@ -35,6 +36,7 @@ PLAN = {
     "C4b32": dict(seqs=list(range(32)), full_seqs=[0, 31]),
     "C5": dict(seqs=[0], full_seqs=[0]),
     "C5bf16": dict(seqs=[0], full_seqs=[0]),
+    "C5w": dict(seqs=[0], full_seqs=[0]),
 }
 
 

@@ -136,3 +136,8 @@ def test_golden_C5():
 @pytest.mark.timeout(900)
 def test_golden_C5_bfloat16():
     _run("C5bf16")
+
+
+@pytest.mark.timeout(900)
+def test_golden_C5_window_past_max_seq():
+    _run("C5w")

@@ -165,6 +165,52 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out
     print(json.dumps(rec))
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE"
+
+
+def summarize_mfma(pmc_dir, workload, out_txt, n_xcd=8, n_simd=1024):
+    """Matrix-core use per kernel of a batched decode bench from one rocprofv3 --pmc
+    run of MFMA_COUNTERS: fp32 matrix flops (SQ_INSTS_VALU_MFMA_MOPS_F32 counts units
+    of 512), and the busy share of the matrix cores, SQ_VALU_MFMA_BUSY_CYCLES over
+    the kernel's cycles (GRBM_GUI_ACTIVE, summed over the XCDs) times the SIMDs."""
+    import collections
+    import csv
+    import glob
+    import re
+    path = glob.glob(os.path.join(pmc_dir, "*_counter_collection.csv"))[0]
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    launches = collections.defaultdict(set)
+    for r in csv.DictReader(open(path)):
+        name = re.sub(r"\(ld::.*", "", r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                      .replace("void ", "").replace("ld::", ""))
+        tot[name][r["Counter_Name"]] += float(r["Counter_Value"])
+        launches[name].add(r["Dispatch_Id"])
+    lines = ["%-46s %7s %16s %14s %11s" % ("kernel", "calls", "MFMA flops/call", "kernel cycles",
+                                           "MFMA busy")]
+    all_busy = all_cyc = 0.0
+    for name, c in sorted(tot.items(), key=lambda kv: -kv[1]["SQ_VALU_MFMA_BUSY_CYCLES"]):
+        if c["SQ_INSTS_VALU_MFMA_MOPS_F32"] == 0:
+            continue
+        n = len(launches[name])
+        cyc = c["GRBM_GUI_ACTIVE"] / n_xcd
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * n_simd)
+        all_busy += c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        all_cyc += cyc
+        lines.append("%-46s %7d %16.4g %14.0f %10.1f%%" % (name[:46], n, 512 * c["SQ_INSTS_VALU_MFMA_MOPS_F32"] / n,
+                                                          cyc / n, 100 * busy))
+    lines.append("all matrix-core kernels: MFMA busy %.1f%% of their cycles" % (100 * all_busy / (all_cyc * n_simd)))
+    with open(out_txt, "w") as fh:
+        fh.write("Matrix-core use per kernel from rocprofv3 counters, workload %s (the run includes the\n"
+                 "prompt's prefill: the LDS-tiled k_gemm launches with few calls).\n"
+                 "command (from the repository root, on an MI355X):\n"
+                 "  rocprofv3 --pmc %s --output-format csv -d %s -o m -- python -u bench.py --workload %s "
+                 "--steps 16 --warmup 2 --no-cpu-baseline\n"
+                 "  python bench.py --summarize-mfma %s %s\n\n"
+                 % (workload, MFMA_COUNTERS, pmc_dir, workload, pmc_dir, workload))
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def gemm_flops_per_step(cfg, batch):
     """Algorithmic flops of every projection of one decode step for `batch` rows."""
     d, f, V, L, kvd = cfg.dim, cfg.hidden_dim, cfg.vocab_size, cfg.n_layers, cfg.kv_dim
@@ -186,10 +232,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("DIR", "WORKLOAD"),
+                    help="a rocprofv3 --pmc run of the MFMA counters on a batched workload: writes "
+                         "the matrix-core use per kernel under profiles/")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
                     help="rocprofv3 --pmc output dirs: FETCH_SIZE and WRITE_SIZE of this bench, "
                          "then of --copy-calibration; writes the traffic summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma[0], args.summarize_mfma[1],
+                       os.path.join(ROOT, "profiles", "mfma_%s.txt" % args.summarize_mfma[1].lower()))
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, TRAFFIC_FILE,
                            os.path.join(ROOT, "profiles", "counters_w13_gemv_7b.txt"))

@@ -677,7 +677,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s, int* nparts) {
     kz = (kz + 31) / 32 * 32;
     ks = (a.K + kz - 1) / kz;
     grid.z = ks;
-    const int kc = kz <= SK_KC ? kz : 256;
+    // a slice deeper than SK_KC is walked in chunks of 256 (whole 32-k steps, never past SK_KC)
+    const int kc = kz <= SK_KC ? kz : std::min(256, SK_KC / 32 * 32);
     const size_t shmem = sk_lds_bytes(kc, a.carry, bn);
     // the staging area may exceed the default 64 KiB dynamic LDS limit (160 KiB per CU on gfx950)
     static bool lds_raised = false;

@@ -74,7 +74,10 @@ __device__ __forceinline__ void merge_unit(const double* pu, int nchunk, int hd,
   out[i] = (float)(acc / l);
 }
 
-template <int HD>
+// SPLIT: the (row, head) units are split into chunks whose partials are merged
+// here; without it every unit is one workgroup (batched decode), and the merge
+// code (and its registers) is left out.
+template <int HD, bool SPLIT>
 __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
   __shared__ double ow[4][kMaxHd];
   __shared__ int is_last;
@@ -88,7 +91,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
   const int nreal = min(nchunk, ntiles);
   if (c >= nreal) return;
   float* out = a.out + (size_t)r * a.d + (size_t)h * HD;
-  if (nreal == 1) {
+  if (!SPLIT || nreal == 1) {
     if (w == 0) {
 #pragma unroll
       for (int k = 0; k < DPL; ++k) {
@@ -98,6 +101,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
     }
     return;
   }
+  if constexpr (!SPLIT) return;
   // split head: publish this chunk's partial (o, m, l), then take a ticket; the
   // last of the nreal chunks of the (row, head) to arrive merges them
   const size_t unit = (size_t)r * a.H + h;
@@ -181,8 +185,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   dim3 grid(nchunk, a.H, a.rows);
   switch (a.hd) {
-#define LD_ATTN_CASE(HD) \
-    case HD: hipLaunchKernelGGL((k_attn<HD>), grid, dim3(kThreads), 0, s, a, nchunk); break;
+#define LD_ATTN_CASE(HD)                                                                    \
+    case HD:                                                                                \
+      if (nchunk > 1) hipLaunchKernelGGL((k_attn<HD, true>), grid, dim3(kThreads), 0, s, a, nchunk); \
+      else hipLaunchKernelGGL((k_attn<HD, false>), grid, dim3(kThreads), 0, s, a, nchunk); \
+      break;
     LD_ATTN_CASE(16) LD_ATTN_CASE(32) LD_ATTN_CASE(48) LD_ATTN_CASE(64) LD_ATTN_CASE(80) LD_ATTN_CASE(96)
     LD_ATTN_CASE(112) LD_ATTN_CASE(128) LD_ATTN_CASE(144) LD_ATTN_CASE(160) LD_ATTN_CASE(176)
     LD_ATTN_CASE(192) LD_ATTN_CASE(208) LD_ATTN_CASE(224) LD_ATTN_CASE(240) LD_ATTN_CASE(256)

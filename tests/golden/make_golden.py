@@ -10,6 +10,10 @@ Those greedy sequences are the teacher-forcing inputs of the GPU parity tests.
     python tests/golden/make_golden.py C5            (~1.5 h, ~30 GB of RAM)
     python tests/golden/make_golden.py C5bf16        (the same with bfloat16 weights)
     python tests/golden/make_golden.py C5w           (past max_seq: ~2.5 h)
+
+GOLDEN_PROCS sets the worker processes (default 6), GOLDEN_THREADS the threads
+each uses to draw its weights (default 4; the draw is counter-based, so the
+weights do not depend on it, and the forward pass is single-threaded).
 """
 import hashlib
 import os
@@ -63,7 +67,7 @@ def prompt_of(w, seq):
 def _run_one(args):
     name, seq, keep = args
     w = WORKLOADS[name]
-    m = O.OracleModel(w.model, w.model_seed, nthreads=4)
+    m = O.OracleModel(w.model, w.model_seed, nthreads=int(os.environ.get("GOLDEN_THREADS", "4")))
     t0 = time.time()
     tin, tout, t1, t2, kept = O.run_sequence(m, prompt_of(w, seq), w.end_pos, keep_logits=keep)
     m.close()

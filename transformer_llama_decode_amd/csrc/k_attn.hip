@@ -170,14 +170,18 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   int nchunk = 1;
   if (units < kSplitBelow) {
     if (a.pos_dev != nullptr) {
-      // position unknown on the host: a fixed split, about 512 workgroups, at
-      // most one chunk per tile of the cache
-      nchunk = std::max(1, std::min(a.seq_pad / kTile, 512 / units));
+      // position unknown on the host: a fixed split, about 256 workgroups, at
+      // most one chunk per tile of the cache (7B decode shape replayed as a graph:
+      // 5.18 ms per step against 5.22 ms with 512)
+      nchunk = std::max(1, std::min(a.seq_pad / kTile, 256 / units));
     } else {
-      // about 256 workgroups: one or two tiles each (measured best at the 7B decode shape)
+      // at most about 256 workgroups, each taking ceil(units * tiles / 256) tiles:
+      // every chunk adds a partial to the merge, which costs more than a second
+      // tile per workgroup (7B decode shape, positions 512..1023: 14.7 us per
+      // layer against 15.5 us with up to 480 one-tile workgroups)
       // slots visited by the longest history among the rows
       const int tiles = (std::min(a.pos + a.n_tok, a.seq_pad) + kTile - 1) / kTile;
-      int per = std::max(1, (units * tiles) / 256);
+      int per = std::max(1, (units * tiles + 255) / 256);
       while ((size_t)units * ((tiles + per - 1) / per) > (size_t)kMaxAttnParts) ++per;
       nchunk = (tiles + per - 1) / per;
     }

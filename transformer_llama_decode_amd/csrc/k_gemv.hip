@@ -94,43 +94,102 @@ __device__ __forceinline__ double dotw(const uint4 w, const XVec8f& x, double ac
   return acc + (double)c;
 }
 
-// Stage x[0..K) into LDS; with a gain, replace it by RMSNorm(x) * gain rounded to fp32.
-__device__ void stage_input(float* xs, const float* __restrict__ x, const float* __restrict__ gain,
-                            int K, double eps, double* red) {
+// Staging x[0..K) into LDS (with a gain: RMSNorm(x) * gain rounded to fp32), in
+// two halves.  stage_issue loads the first XB float4 of each thread's share of x
+// (and, for NORM, of the gains) into registers, all at once and unpredicated
+// (indices past the end re-read the last element, unused), so they share one
+// round trip; stage_finish takes the sum of squares and stores the (normalised)
+// vector.  Elements past XB * kThreads float4 (only for K above 4 * XB * kThreads)
+// are loaded in stage_finish.
+template <int XB>
+struct XStage {
+  float4 x[XB], g[XB];
+};
+
+template <int XB, bool NORM>
+__device__ __forceinline__ void stage_issue(XStage<XB>& r, const float* __restrict__ x,
+                                            const float* __restrict__ gain, int K) {
+  const int tid = threadIdx.x, K4 = K >> 2;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  const float4* g4 = reinterpret_cast<const float4*>(gain != nullptr ? gain : x);
+#pragma unroll
+  for (int u = 0; u < XB; ++u) {
+    const int j = min(tid + u * kThreads, K4 - 1);
+    r.x[u] = x4[j];
+    if (NORM) r.g[u] = g4[j];
+  }
+}
+
+__device__ __forceinline__ double sumsq4(float4 v, double ss) {
+  ss = fma((double)v.x, (double)v.x, ss);
+  ss = fma((double)v.y, (double)v.y, ss);
+  ss = fma((double)v.z, (double)v.z, ss);
+  return fma((double)v.w, (double)v.w, ss);
+}
+
+__device__ __forceinline__ float4 norm4(float4 v, double inv, float4 g) {
+  v.x = (float)((double)v.x * inv * (double)g.x);
+  v.y = (float)((double)v.y * inv * (double)g.y);
+  v.z = (float)((double)v.z * inv * (double)g.z);
+  v.w = (float)((double)v.w * inv * (double)g.w);
+  return v;
+}
+
+template <int XB>
+__device__ void stage_finish(float* xs, const XStage<XB>& r, const float* __restrict__ x,
+                             const float* __restrict__ gain, int K, double eps, double* red) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K4 = K >> 2;
   const float4* x4 = reinterpret_cast<const float4*>(x);
   float4* xs4 = reinterpret_cast<float4*>(xs);
+  constexpr int kEarly = XB * kThreads;   // float4 slots loaded by stage_issue
   if (gain == nullptr) {
-    for (int j = tid; j < K4; j += kThreads) xs4[j] = x4[j];
+#pragma unroll
+    for (int u = 0; u < XB; ++u)
+      if (tid + u * kThreads < K4) xs4[tid + u * kThreads] = r.x[u];
+    for (int j = tid + kEarly; j < K4; j += kThreads) xs4[j] = x4[j];
     __syncthreads();
     return;
   }
+  // the sum of squares in the same order as one pass over j = tid, tid + kThreads, ...
   double ss = 0.0;
-  for (int j = tid; j < K4; j += kThreads) {
-    float4 v = x4[j];
+#pragma unroll
+  for (int u = 0; u < XB; ++u)
+    if (tid + u * kThreads < K4) ss = sumsq4(r.x[u], ss);
+  for (int j = tid + kEarly; j < K4; j += kThreads) {
+    const float4 v = x4[j];
     xs4[j] = v;
-    ss = fma((double)v.x, (double)v.x, ss);
-    ss = fma((double)v.y, (double)v.y, ss);
-    ss = fma((double)v.z, (double)v.z, ss);
-    ss = fma((double)v.w, (double)v.w, ss);
+    ss = sumsq4(v, ss);
   }
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   const double tot = ((red[0] + red[1]) + red[2]) + red[3];
   const double inv = 1.0 / sqrt(tot / (double)K + eps);
+#pragma unroll
+  for (int u = 0; u < XB; ++u)
+    if (tid + u * kThreads < K4) xs4[tid + u * kThreads] = norm4(r.x[u], inv, r.g[u]);
   const float4* g4 = reinterpret_cast<const float4*>(gain);
-  for (int j = tid; j < K4; j += kThreads) {
-    float4 v = xs4[j];
-    const float4 g = g4[j];
-    v.x = (float)((double)v.x * inv * (double)g.x);
-    v.y = (float)((double)v.y * inv * (double)g.y);
-    v.z = (float)((double)v.z * inv * (double)g.z);
-    v.w = (float)((double)v.w * inv * (double)g.w);
-    xs4[j] = v;
-  }
+  for (int j = tid + kEarly; j < K4; j += kThreads) xs4[j] = norm4(xs4[j], inv, g4[j]);
   __syncthreads();
+}
+
+// An empty register barrier on the first weight batch: its conversions to fp64
+// cannot be moved above this point, so the wait for the batch stays behind the
+// prologue (hipcc otherwise converts right after the loads, waiting for HBM there).
+template <int NR, int U>
+__device__ __forceinline__ void hold_batch(float4 (&w)[U][NR]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(w[u][r].x), "+v"(w[u][r].y), "+v"(w[u][r].z), "+v"(w[u][r].w));
+}
+template <int NR, int U>
+__device__ __forceinline__ void hold_batch(uint4 (&w)[U][NR]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(w[u][r].x), "+v"(w[u][r].y), "+v"(w[u][r].z), "+v"(w[u][r].w));
 }
 
 template <int NR, int U, bool NT, typename T>
@@ -222,7 +281,9 @@ __device__ __forceinline__ double pick(const double (&acc)[N], int i) {
 //              groups are in flight per wave.
 enum Mode { MODE_PLAIN = 0, MODE_PIPE = 1, MODE_DB = 2 };
 
-template <int EPI, int RW, int U, bool NT, bool BF, int MODE>
+// BIG: rows of at least one batch (U * 64 weight vectors); the first batch is
+// then loaded before the prologue.  Shorter rows (small models) skip it.
+template <int EPI, int RW, int U, bool NT, bool BF, int MODE, bool BIG>
 __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   static_assert(EPI != EPI_QKV || RW % 2 == 0, "a rotary pair's two rows sit in one row group");
   typedef typename WVec<BF>::T T;
@@ -257,19 +318,34 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   };
 
   // The weights do not depend on the input vector: issue the first batch of
-  // this wave's loads before staging (and normalising) x, so the prologue
-  // overlaps the first HBM round trip.
+  // this wave's loads before staging (and normalising) x, then every x and gain
+  // load at once, so the prologue costs one round trip, overlapped with the
+  // batch's.
   int grp = blockIdx.x * kWavesPerBlock + wave;
   const T* rows[NR];
   set_rows(rows, grp * RW);
   T wpre[U][NR];
-  bool pre = grp < ngroups && (KV >> 6) >= U;
-  if (pre) load_batch<NR, U, NT>(wpre, rows, 0, lane);
+  bool pre = false;
+  if constexpr (BIG) {
+    // unpredicated (a branch would make the compiler copy the registers as they
+    // arrive, waiting for HBM right here): a wave without a group loads rows
+    // that exist (set_rows clamps them) and does not use them
+    pre = grp < ngroups;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) wpre[u][r] = ld_w<NT>(rows[r] + u * kWave + lane);
+  }
+  // x float4 per thread loaded at once (W2's input is the FFN width)
+  constexpr int XB = !BIG ? 2 : (EPI == EPI_RESID) ? 12 : 8;
+  XStage<XB> xr;
+  stage_issue<XB, EPI != EPI_RESID>(xr, a.x, a.gain, K);
 
   // position of the token (rotary angle, KV-cache slot); first needed by the
   // first row group's epilogue fetch, so the load overlaps the prologue
   const int pos = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
-  stage_input(xs, a.x, a.gain, K, a.eps, red);
+  stage_finish<XB>(xs, xr, a.x, a.gain, K, a.eps, red);
+  if constexpr (BIG) hold_batch<NR, U>(wpre);
   const float4* xs4 = reinterpret_cast<const float4*>(xs);
 
   // Lane i finishes row r0 + i.  What its epilogue reads (the residual element,
@@ -411,19 +487,26 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   }
 }
 
-template <int EPI, int RW, int U, bool NT, bool BF, int MODE>
-hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blocks_out) {
+template <int EPI, int RW, int U, bool NT, bool BF, int MODE, bool BIG>
+hipError_t launch_cfg2(const GemvArgs& a, int max_blocks, hipStream_t s, int* blocks_out) {
   const int groups = (a.N + RW - 1) / RW;
   int blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks_out) *blocks_out = blocks;
   const size_t shmem = (size_t)a.K * sizeof(float);
   if (a.ev_start != nullptr)
-    hipExtLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE>), dim3(blocks), dim3(kThreads), shmem, s, a.ev_start,
-                          a.ev_stop, 0, a);
+    hipExtLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE, BIG>), dim3(blocks), dim3(kThreads), shmem, s,
+                          a.ev_start, a.ev_stop, 0, a);
   else
-    hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE>), dim3(blocks), dim3(kThreads), shmem, s, a);
+    hipLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE, BIG>), dim3(blocks), dim3(kThreads), shmem, s, a);
   return hipGetLastError();
+}
+
+template <int EPI, int RW, int U, bool NT, bool BF, int MODE>
+hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blocks_out) {
+  if (a.K / WVec<BF>::E / kWave >= U) return launch_cfg2<EPI, RW, U, NT, BF, MODE, true>(a, max_blocks, s, blocks_out);
+  if constexpr (MODE == MODE_DB) return hipErrorInvalidValue;   // rows of exactly one batch
+  else return launch_cfg2<EPI, RW, U, NT, BF, MODE, false>(a, max_blocks, s, blocks_out);
 }
 
 // Streamed (non-temporal) loads once the model's weights are too big to stay

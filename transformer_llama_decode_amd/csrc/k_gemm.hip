@@ -14,7 +14,7 @@
 //  * bfloat16 weights are widened to fp32 (exactly) as they are loaded, so the
 //    LDS tiles and the matrix-core arithmetic are those of fp32 weights;
 //  * accumulation is fp32 in the matrix cores.  For wide models the fp32
-//    partial sums are carried into fp64 registers after every K step of 32, so
+//    partial sums are carried into fp64 registers after every 16 k, so
 //    the rounding error does not grow with K;
 //  * epilogues are fused: rotary embedding + KV-cache write for Q/K/V (pairs sit
 //    in adjacent lanes), residual add for Wo and W2, the SwiGLU gate for W1/W3
@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   constexpr int LS = lds_stride<KS>();
   constexpr int AL = (BM * (KS / 4) + NTHR - 1) / NTHR;
   constexpr int BL = (BN * (KS / 4) + NTHR - 1) / NTHR;
-  static_assert(!CARRY || KS == 32, "fp64 carries every 32 k");
+  static_assert(!CARRY || KS == 32, "fp64 carries every 16 k, two per K step");
   __shared__ float As[2][BM * LS];
   __shared__ float Bs[2][BN * LS];
 
@@ -184,17 +184,17 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt].z, bv[nt].z, acc[mt][nt], 0, 0, 0);
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt].w, bv[nt].w, acc[mt][nt], 0, 0, 0);
         }
-    }
-    if (CARRY) {
+      if (CARRY && (kk & 8)) {   // after every 16 k (kk = 8, 24)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            dacc[mt][nt][j & (CARRY ? 15 : 0)] += (double)acc[mt][nt][j];
-            acc[mt][nt][j] = 0.f;
-          }
+            for (int j = 0; j < 16; ++j) {
+              dacc[mt][nt][j & (CARRY ? 15 : 0)] += (double)acc[mt][nt][j];
+              acc[mt][nt][j] = 0.f;
+            }
+      }
     }
     if (more) {
       tile_sstore<BM, NTHR, false, AL, KS>(ra, As[cur ^ 1], tid);
@@ -472,6 +472,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
     sstore(kn);
     __syncthreads();
     if (kb + kc < kend) gload(kb + kc, min(kc, kend - kb - kc));   // in flight while this chunk is used
+    int ng = 0;   // 8-k groups since the last carry
     for (int g = w; g < (kn >> 3); g += KW) {
       const float4 av = *reinterpret_cast<const float4*>(stg + row * ldsw + 8 * g + kofs);
       const float4 b0 = *reinterpret_cast<const float4*>(stg + (32 + row) * ldsw + 8 * g + kofs);
@@ -486,8 +487,18 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
         acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b1.z, acc1, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b1.w, acc1, 0, 0, 0);
       }
+      if (CARRY && ++ng == 2) {   // into fp64 after every 16 k of this wave
+        ng = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          dacc[0][j & (CARRY ? 15 : 0)] += (double)acc0[j];
+          dacc[1][j & (CARRY ? 15 : 0)] += (double)acc1[j];
+          acc0[j] = 0.f;
+          acc1[j] = 0.f;
+        }
+      }
     }
-    if (CARRY) {   // at most kc / 8 / KW = 5 groups (40 k) per wave per chunk in fp32
+    if (CARRY && ng != 0) {   // the chunk's last odd group
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         dacc[0][j & (CARRY ? 15 : 0)] += (double)acc0[j];

@@ -44,9 +44,19 @@ def build_oracle(src=ORACLE_SRC, out=ORACLE_LIB, extra=()):
     return out
 
 
+ORACLE_TIMING_LIB = os.path.join(ROOT, "oracle", "liboracle_accf.so")
+
+
+def build_oracle_timing():
+    """The timing-only build with float accumulators (-DOR_ACC=float): the pages'
+    plain fp32 C loop, for the CPU baseline's comparison; never used for parity."""
+    return build_oracle(out=ORACLE_TIMING_LIB, extra=("-DOR_ACC=float",))
+
+
 def build():
     build_synth()
     build_oracle()
+    build_oracle_timing()
 
 
 if __name__ == "__main__":

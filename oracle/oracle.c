@@ -37,13 +37,22 @@
 
 #include "synth.h"
 
+/* Accumulator of the dot products and sums of squares.  The oracle proper is
+ * built with double (the precision policy of oracle.h); a timing-only build
+ * with -DOR_ACC=float sums in float instead, as the pages' own plain fp32 C
+ * loop does, and is never used to check results. */
+#ifndef OR_ACC
+#define OR_ACC double
+#endif
+typedef OR_ACC or_acc;
+
 /* ------------------------------------------------------------------ ops -- */
 
 /* RMSNorm (Zhang & Sennrich 2019, eq. 4): y_i = x_i / sqrt(mean(x^2) + eps) * g_i */
 void or_rmsnorm(float* out, const float* x, const float* gain, int n, double eps) {
-  double ss = 0.0;
-  for (int i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
-  double inv = 1.0 / sqrt(ss / (double)n + eps);
+  or_acc ss = 0;
+  for (int i = 0; i < n; ++i) ss += (or_acc)x[i] * (or_acc)x[i];
+  double inv = 1.0 / sqrt((double)ss / (double)n + eps);
   for (int i = 0; i < n; ++i) out[i] = (float)((double)x[i] * inv * (double)gain[i]);
 }
 
@@ -51,8 +60,8 @@ void or_rmsnorm(float* out, const float* x, const float* gain, int n, double eps
 void or_matvec(float* out, const float* w, const float* x, int rows, int cols) {
   for (int r = 0; r < rows; ++r) {
     const float* row = w + (size_t)r * (size_t)cols;
-    double acc = 0.0;
-    for (int k = 0; k < cols; ++k) acc += (double)row[k] * (double)x[k];
+    or_acc acc = 0;
+    for (int k = 0; k < cols; ++k) acc += (or_acc)row[k] * (or_acc)x[k];
     out[r] = (float)acc;
   }
 }
@@ -137,15 +146,15 @@ void or_attention(float* out, const float* q, const float* k_rows, const float* 
     const size_t kv_off = (size_t)(h / group) * hd;
     for (int j = 0; j < n_pos; ++j) {
       const float* kj = k_rows + (size_t)j * kvd + kv_off;
-      double dot = 0.0;
-      for (int i = 0; i < hd; ++i) dot += (double)qh[i] * (double)kj[i];
-      s[j] = dot / sqrt((double)hd);
+      or_acc dot = 0;
+      for (int i = 0; i < hd; ++i) dot += (or_acc)qh[i] * (or_acc)kj[i];
+      s[j] = (double)dot / sqrt((double)hd);
     }
     or_softmax(s, n_pos);
     for (int i = 0; i < hd; ++i) {
-      double acc = 0.0;
+      or_acc acc = 0;
       for (int j = 0; j < n_pos; ++j)
-        acc += s[j] * (double)v_rows[(size_t)j * kvd + kv_off + i];
+        acc += (or_acc)s[j] * (or_acc)v_rows[(size_t)j * kvd + kv_off + i];
       out[(size_t)h * hd + i] = (float)acc;
     }
   }

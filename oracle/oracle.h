@@ -7,11 +7,15 @@
  * code with the HIP library except the seeded input generator (synth/).
  *
  * Precision policy: every tensor is STORED in fp32 (as in the pages' engine,
- * which "currently only supports fp32": openai.wiki "llama2.c | Baby LLaMA",
+ * which handles fp32 only: openai.wiki "llama2.c | Baby LLaMA",
  * intro), and every reduction (dot products, sum of squares, softmax sums,
  * attention-weighted sums) is ACCUMULATED in double.  Products of two fp32
  * values are exact in double, so each stored result is the correctly rounded
  * value up to ~1e-16 relative, independent of summation order.
+ *
+ * Built with -DOR_ACC=float (a timing-only build of the CPU baseline, never
+ * used to check results) the dot products, sums of squares and weighted sums
+ * accumulate in float instead, like the pages' plain fp32 C loop.
  */
 #ifndef LD_ORACLE_H
 #define LD_ORACLE_H

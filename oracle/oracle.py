@@ -251,14 +251,16 @@ class OracleState:
             pass
 
 
-def run_sequence(model, prompt, n_positions, feed=None, keep_logits=None):
+def run_sequence(model, prompt, n_positions, feed=None, keep_logits=None, sub_idx=None):
     """Greedy run of one sequence through positions 0..n_positions-1.
 
     Position p < len(prompt) consumes prompt[p]; later positions consume the
     previous position's greedy token, or feed[p] when `feed` (teacher tokens,
     indexed by position) is given.  Returns (tokens_in[n_positions],
     greedy_out[n_positions], top1_val, top2_val, kept) where `kept` maps each
-    position in `keep_logits` to its full logits vector.
+    position in `keep_logits` to its full logits vector.  With `sub_idx` (logit
+    indices), kept["sub"] is also an [n_positions, len(sub_idx)] array of those
+    logits at every position.
     """
     st = model.new_state()
     V = model.cfg.vocab_size
@@ -269,6 +271,11 @@ def run_sequence(model, prompt, n_positions, feed=None, keep_logits=None):
     kept = {}
     keep = set(keep_logits or ())
     logits = np.empty(V, np.float32)
+    sub = None
+    if sub_idx is not None:
+        sub_idx = np.asarray(sub_idx, np.int64)
+        sub = np.zeros((n_positions, sub_idx.size), np.float32)
+        kept["sub"] = sub
     nxt = None
     for p in range(n_positions):
         if p < len(prompt):
@@ -288,5 +295,7 @@ def run_sequence(model, prompt, n_positions, feed=None, keep_logits=None):
         top2[p] = masked.max()
         if p in keep:
             kept[p] = logits.copy()
+        if sub is not None:
+            sub[p] = logits[sub_idx]
         nxt = r
     return tin, tout, top1, top2, kept

@@ -3,8 +3,11 @@
 Calls only oracle/ (and the shared input generator through it).  For each
 workload and each stored sequence it runs the oracle greedily over every
 position and records, per position: the token fed in, the greedy token out, the
-top-1 and top-2 logit values; and the full logit vector at a few positions.
-Those greedy sequences are the teacher-forcing inputs of the GPU parity tests.
+top-1 and top-2 logit values.  For the sequences listed in `full_seqs` it also
+records the full logit vector at the last prompt position, the two after it,
+every 32nd position after it and the last two, and a fixed set of SUB_N logit indices
+(drawn once from SUB_SEED, stored with the file) at every position.  Those greedy
+sequences are the teacher-forcing inputs of the GPU parity tests.
 
     python tests/golden/make_golden.py C2 C3 ...     (default: all but C5)
     python tests/golden/make_golden.py C5            (~1.5 h, ~30 GB of RAM)
@@ -52,10 +55,21 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+# logit indices stored at every position: SUB_N distinct indices from a fixed seed
+SUB_N, SUB_SEED, FULL_EVERY = 256, 20240, 32
+
+
+def sub_indices(V):
+    return np.sort(np.random.default_rng(SUB_SEED).choice(V, SUB_N, replace=False)).astype(np.int32)
+
+
 def keep_positions(w):
+    """Positions whose full logits are stored: the last prompt position (the
+    first one the GPU is compared at), every FULL_EVERY-th position after it,
+    the two after the prompt and the last two."""
     P = max(w.prompt_len, 1)
     E = w.end_pos
-    return sorted({P - 1, P, P + 1, (P + E) // 2, E - 1})
+    return sorted(set(range(P - 1, E, FULL_EVERY)) | {P, P + 1, E - 2, E - 1})
 
 
 def prompt_of(w, seq):
@@ -69,7 +83,9 @@ def _run_one(args):
     w = WORKLOADS[name]
     m = O.OracleModel(w.model, w.model_seed, nthreads=int(os.environ.get("GOLDEN_THREADS", "4")))
     t0 = time.time()
-    tin, tout, t1, t2, kept = O.run_sequence(m, prompt_of(w, seq), w.end_pos, keep_logits=keep)
+    sub = sub_indices(w.model.vocab_size) if keep else None
+    tin, tout, t1, t2, kept = O.run_sequence(m, prompt_of(w, seq), w.end_pos, keep_logits=keep,
+                                             sub_idx=sub)
     m.close()
     return seq, tin, tout, t1, t2, kept, time.time() - t0
 
@@ -85,21 +101,28 @@ def make(name, procs):
     top1 = np.zeros((n, w.end_pos), np.float32)
     top2 = np.zeros((n, w.end_pos), np.float32)
     full = {}
+    subs = {}
     t0 = time.time()
     with ProcessPoolExecutor(max_workers=min(procs, n)) as ex:
         for k, (seq, a, b, c, d, kept, dt) in enumerate(ex.map(_run_one, jobs)):
             i = plan["seqs"].index(seq)
             tin[i], tout[i], top1[i], top2[i] = a, b, c, d
             for p, v in kept.items():
-                full[(seq, p)] = v
+                if p == "sub":
+                    subs[seq] = v
+                else:
+                    full[(seq, p)] = v
             print("%s seq %d done (%.1fs, %d/%d)" % (name, seq, dt, k + 1, n), flush=True)
     fs = sorted(full)
+    ss = sorted(subs)
     out = os.path.join(HERE, "%s.npz" % name)
     np.savez_compressed(
         out, workload=np.array(name), source_hash=np.array(source_hash()),
         seqs=np.array(plan["seqs"], np.int32), tokens_in=tin, greedy=tout, top1=top1, top2=top2,
         full_seq=np.array([s for s, _ in fs], np.int32), full_pos=np.array([p for _, p in fs], np.int32),
-        full_logits=np.stack([full[k] for k in fs]) if fs else np.zeros((0, w.model.vocab_size), np.float32))
+        full_logits=np.stack([full[k] for k in fs]) if fs else np.zeros((0, w.model.vocab_size), np.float32),
+        sub_idx=sub_indices(w.model.vocab_size), sub_seq=np.array(ss, np.int32),
+        sub_logits=np.stack([subs[k] for k in ss]) if ss else np.zeros((0, w.end_pos, SUB_N), np.float32))
     print("wrote %s in %.0fs" % (out, time.time() - t0), flush=True)
 
 

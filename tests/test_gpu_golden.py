@@ -3,13 +3,18 @@
 tests/golden/<workload>.npz are written by tests/golden/make_golden.py, which
 calls only the oracle: for every stored sequence and position, the token fed
 in (the oracle's own greedy stream, used here for teacher forcing), the greedy
-token out, the top-1 and top-2 logit values, and full logit vectors at a few
-positions.  The GPU runs the workload in the configuration the benchmark times
-(prefill of the prompt, then lockstep decode steps) and is checked on:
-  * every logit at the stored positions (tolerance of tests/parity.py);
-  * at every position: the GPU logit at the oracle's arg-max index against the
-    oracle's top-1 value, and the greedy token where the oracle's top-1 margin
-    exceeds 1e-3.
+token out, the top-1 and top-2 logit values; for one or two sequences, full
+logit vectors at the last prompt position and every 32nd position after it,
+and a fixed set of 256 logit indices at every position.  The GPU runs the
+workload in the configuration the benchmark times (prefill of the prompt, then
+lockstep decode steps) and is checked, at every compared position (the last
+prompt position and every decode step), on:
+  * every logit where the full vector is stored (tolerance of tests/parity.py);
+  * the stored subset of logit indices;
+  * the GPU logit at the oracle's arg-max index against the oracle's top-1
+    value, and the greedy token where the oracle's top-1 margin exceeds 1e-3.
+Failures are collected over all positions (not stopped at the first), and the
+worst |gpu - oracle| / tolerance of each kind is printed.
 """
 import hashlib
 import os
@@ -19,7 +24,7 @@ import numpy as np
 import pytest
 
 from transformer_llama_decode_amd.configs import WORKLOADS
-from tests.parity import REL, ABS, MARGIN, assert_logits
+from tests.parity import REL, ABS, MARGIN
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -62,7 +67,10 @@ def _run(name, gold_name=None, seqs=None):
     tin, greedy = z["tokens_in"][rows], z["greedy"][rows]
     top1, top2 = z["top1"][rows], z["top2"][rows]
     full = {(int(s), int(p)): z["full_logits"][i] for i, (s, p) in enumerate(zip(z["full_seq"], z["full_pos"]))}
+    sub_idx = z["sub_idx"].astype(np.int64) if "sub_idx" in z.files else None
+    subs = {int(s): z["sub_logits"][i] for i, s in enumerate(z["sub_seq"])} if sub_idx is not None else {}
     seq_ids = [allseqs[r] for r in rows]
+    sub_rows = [bi for bi, s in enumerate(seq_ids) if s in subs]
     dev = torch.device("cuda", 0)
     _say("%s: init model (B=%d)" % (name, B))
     gm = LlamaDecoder(w.model, w.model_seed)
@@ -70,23 +78,49 @@ def _run(name, gold_name=None, seqs=None):
     P = max(w.prompt_len, 1)
     logits = torch.empty((B, V), dtype=torch.float32, device=dev)
     idx_top = torch.from_numpy(greedy.astype(np.int64)).to(dev)      # [B, E]
+    sub_dev = torch.from_numpy(sub_idx).to(dev) if sub_rows else None
     ar = torch.arange(B, device=dev)
     fails = []
+    worst = {"full": 0.0, "sub": 0.0, "top1": 0.0}
+    counts = {"full": 0, "sub": 0, "top1": 0, "positions": 0}
+
+    def ratio(g, o):
+        g = np.asarray(g, np.float64)
+        o = np.asarray(o, np.float64)
+        return np.abs(g - o) / np.maximum(REL * np.abs(o), ABS)
 
     def check(p, nxt):
-        got_top = logits[ar, idx_top[:, p]].cpu().numpy().astype(np.float64)
-        want = top1[:, p].astype(np.float64)
-        bad = np.abs(got_top - want) > np.maximum(REL * np.abs(want), ABS)
-        if bad.any():
-            fails.append("pos %d: top-1 value off for %d seqs" % (p, int(bad.sum())))
+        counts["positions"] += 1
+        got_top = logits[ar, idx_top[:, p]].cpu().numpy()
+        r = ratio(got_top, top1[:, p])
+        worst["top1"] = max(worst["top1"], float(r.max()))
+        counts["top1"] += r.size
+        if (r > 1.0).any():
+            fails.append("pos %d: top-1 value off for %d seqs (worst %.3g x tol)" % (p, int((r > 1).sum()), r.max()))
         nn = nxt.cpu().numpy()
         margin = top1[:, p] - top2[:, p]
         wrong = (margin > MARGIN) & (nn != greedy[:, p])
         if wrong.any():
             fails.append("pos %d: greedy token differs for %d seqs" % (p, int(wrong.sum())))
+        if sub_rows:
+            got = logits[sub_rows][:, sub_dev].cpu().numpy()
+            for j, bi in enumerate(sub_rows):
+                r = ratio(got[j], subs[seq_ids[bi]][p])
+                worst["sub"] = max(worst["sub"], float(r.max()))
+                counts["sub"] += r.size
+                if (r > 1.0).any():
+                    fails.append("%s seq %d pos %d: %d of %d stored-subset logits out of tolerance (worst %.3g x)"
+                                 % (name, seq_ids[bi], p, int((r > 1).sum()), r.size, r.max()))
         for bi, s in enumerate(seq_ids):
             if (s, p) in full:
-                assert_logits(logits[bi].cpu().numpy(), full[(s, p)], "%s seq %d pos %d" % (name, s, p))
+                g = logits[bi].cpu().numpy()
+                r = ratio(g, full[(s, p)])
+                worst["full"] = max(worst["full"], float(r.max()))
+                counts["full"] += r.size
+                if (r > 1.0).any():
+                    i = int(np.argmax(r))
+                    fails.append("%s seq %d pos %d: %d of %d logits out of tolerance; worst at %d: gpu %.9g oracle %.9g"
+                                 % (name, s, p, int((r > 1).sum()), r.size, i, g[i], full[(s, p)][i]))
 
     if w.prompt_len > 0:
         _say("%s: prefill %d x %d" % (name, B, P))
@@ -99,6 +133,10 @@ def _run(name, gold_name=None, seqs=None):
             _say("%s: pos %d" % (name, p))
     assert gm.status() == 0
     gm.close()
+    _say("%s parity margin: worst |gpu - oracle| / tol  full %.3f (%d logits)  subset %.3f (%d)  top-1 %.3f (%d); "
+         "%d positions, %d failures"
+         % (name, worst["full"], counts["full"], worst["sub"], counts["sub"], worst["top1"], counts["top1"],
+            counts["positions"], len(fails)))
     assert not fails, fails[:10]
 
 

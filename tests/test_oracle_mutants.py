@@ -19,12 +19,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTANTS = {
-    "rmsnorm_eps_outside_root": ("1.0 / sqrt(ss / (double)n + eps)", "1.0 / (sqrt(ss / (double)n) + eps)"),
-    "rmsnorm_sum_not_mean": ("ss / (double)n + eps", "ss + eps"),
+    "rmsnorm_eps_outside_root": ("1.0 / sqrt((double)ss / (double)n + eps)",
+                                 "1.0 / (sqrt((double)ss / (double)n) + eps)"),
+    "rmsnorm_sum_not_mean": ("(double)ss / (double)n + eps", "(double)ss + eps"),
     "rmsnorm_gain_dropped": ("* inv * (double)gain[i]", "* inv"),
-    "matvec_transposed": ("acc += (double)row[k] * (double)x[k];",
-                          "acc += (double)w[(size_t)k * rows + r % cols] * (double)x[k % rows];"),
-    "matvec_float_accumulator": ("    double acc = 0.0;\n    for (int k = 0; k < cols; ++k)",
+    "matvec_transposed": ("acc += (or_acc)row[k] * (or_acc)x[k];",
+                          "acc += (or_acc)w[(size_t)k * rows + r % cols] * (or_acc)x[k % rows];"),
+    "matvec_float_accumulator": ("    or_acc acc = 0;\n    for (int k = 0; k < cols; ++k)",
                                  "    float acc = 0.0f;\n    for (int k = 0; k < cols; ++k)"),
     "rope_sign": ("(float)(a * c - b * s)", "(float)(a * c + b * s)"),
     "rope_second_sign": ("(float)(a * s + b * c)", "(float)(-a * s + b * c)"),
@@ -32,7 +33,7 @@ MUTANTS = {
                               "double a = vh[i], b = vh[i + half];"),
     "rope_frequency_exponent": ("-(2.0 * (double)i) / (double)head_dim", "-(double)i / (double)head_dim"),
     "rope_not_applied_to_k": ("    or_rope(s->k, kvd, hd,", "    if (0) or_rope(s->k, kvd, hd,"),
-    "attention_scale_1_over_hd": ("dot / sqrt((double)hd)", "dot / (double)hd"),
+    "attention_scale_1_over_hd": ("(double)dot / sqrt((double)hd)", "(double)dot / (double)hd"),
     "attention_excludes_current_position": ("vl + (size_t)lo * kvd, pos - lo + 1, d,",
                                             "vl + (size_t)lo * kvd, pos - lo > 0 ? pos - lo : 1, d,"),
     "window_one_too_wide": ("int lo = pos - c->max_seq + 1 > 0 ? pos - c->max_seq + 1 : 0;",

@@ -48,13 +48,13 @@ extern "C" {
 #define LD_E_ARENA -3     /* arena too small or misaligned */
 #define LD_E_HIP -4       /* a HIP runtime call failed */
 #define LD_E_NONFINITE -5 /* a logit was NaN or infinite, or a device token was out of range */
-#define LD_E_STATE -6     /* call not valid in the handle's state */
 
 typedef struct {
-  int32_t dim;             /* model width d; multiple of 32 */
+  int32_t dim;             /* model width d; multiple of 32, at most 16384 */
   int32_t n_layers;        /* L */
   int32_t n_heads;         /* H; head_dim = dim / n_heads, a multiple of 16, <= 256 */
-  int32_t hidden_dim;      /* SwiGLU width f; multiple of 32 */
+  int32_t hidden_dim;      /* SwiGLU width f; multiple of 32, at most 39936 (the batch-1 W2
+                              projection stages its whole input in 156 KiB of LDS) */
   int32_t vocab_size;      /* V */
   int32_t max_seq;         /* positions held by the KV cache (the attention window) */
   int32_t max_batch;       /* sequences decoded in lockstep, >= 1 */
@@ -142,7 +142,12 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
 int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* tokens,
                 int32_t tokens_on_device, float* dev_logits, int32_t* dev_out);
 
-/* Forget the cached sequence: pos := 0. */
+/* Start a new sequence: pos := 0.  The KV cache is not cleared (no call reads a
+ * slot before the current sequence writes it).  Each run of the pages' engine
+ * generates from position 0 with an empty cache after loading the checkpoint
+ * (openai.wiki "llama2.c | Baby LLaMA", section "Model inference"); this is that
+ * start without reloading the weights.  Never fails for a valid handle
+ * (LD_E_INVAL for NULL); asynchronous work already queued is unaffected. */
 int ld_kv_reset(ld_model* m);
 
 /* Rewind: pos := new_pos, 0 <= new_pos <= current pos (positions >= new_pos
@@ -151,6 +156,11 @@ int ld_kv_reset(ld_model* m);
  * cache's slots per sequence) once pos > ring. */
 int ld_set_pos(ld_model* m, int32_t new_pos);
 
+/* *pos := the handle's position counter: the number of positions the cache
+ * holds for the current sequence, i.e. the position the next ld_decode_step
+ * computes (the position argument of the pages' per-token forward pass,
+ * openai.wiki "llama2.c | Baby LLaMA", section "Model inference").  Host-side
+ * only: no stream work.  LD_E_INVAL for a NULL handle or pointer. */
 int ld_get_pos(const ld_model* m, int32_t* pos);
 
 /* Copy elements [start, start+n) of weight tensor `stream_id` (synth stream
@@ -158,7 +168,11 @@ int ld_get_pos(const ld_model* m, int32_t* pos);
  * weights widened exactly).  Synchronous. */
 int ld_read_weights(ld_model* m, int64_t stream_id, uint64_t start, uint64_t n, float* host_out);
 
-/* Checksum of every weight matrix as held on the device: the sum, modulo 2^64,
+/* The pages' engine reads its weights from a checkpoint file (openai.wiki
+ * "llama2.c | Baby LLaMA", sections "Environment setup" and "Model inference");
+ * here they are drawn from a seed, and this call proves that the device holds
+ * exactly the draw a reference makes from the same seed.
+ * Checksum of every weight matrix as held on the device: the sum, modulo 2^64,
  * of the 32-bit patterns of all elements of E, Wq, Wk, Wv, Wo, W1, W2, W3 of
  * every layer and the untied classifier (bfloat16 elements widened to fp32
  * first).  Order-free, so a reference computes it from the tensors in any
@@ -189,7 +203,14 @@ int ld_profile_read(ld_model* m, int32_t kernel_class, double* avg_ms, int64_t* 
 int ld_synth_prompt(uint64_t seed, uint64_t seq, int32_t n, int32_t lo, int32_t hi,
                     int32_t* host_out);
 
+/* Release the host-side handle and the library's own stream, events, pinned
+ * host buffers and captured graph, after waiting for the model's stream.  The
+ * caller's arena and output buffers are never freed.  NULL is a no-op.  (The
+ * pages' engine releases its buffers when the one-shot program ends: openai.wiki
+ * "llama2.c | Baby LLaMA", section "Model inference".) */
 void ld_model_free(ld_model* m);
+
+/* Static text for an LD_* code; "unknown error" for any other value. */
 const char* ld_strerror(int code);
 
 #ifdef __cplusplus

@@ -65,6 +65,10 @@ CASES = [
     # bfloat16 weights
     (TINY_BF16, 23),
     (SMALL_BF16, 24),
+    # a long FFN: the batch-1 W2 projection stages 20480 inputs (80 KiB) in LDS,
+    # past the default 64 KiB dynamic limit
+    (ModelConfig(dim=64, n_layers=2, n_heads=4, hidden_dim=20480, vocab_size=301, max_seq=24,
+                 max_batch=3), 25),
 ]
 
 
@@ -264,6 +268,37 @@ def test_error_paths_leave_state_unchanged(dev):
         gm.set_pos(cfg.max_seq + 1)
     gm.set_pos(10)
     assert gm.pos == 10
+    assert gm.status() == 0
+    gm.close()
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_poisoned_weight_is_reported(dev, batch):
+    """a NaN planted in one embedding row reaches exactly one logit through the
+    tied classifier; the classifier's non-finite check must report it"""
+    from transformer_llama_decode_amd._lib import LD_E_NONFINITE
+    cfg, seed = TINY, 6
+    gm, _ = _models(cfg, seed)
+    V, d = cfg.vocab_size, cfg.dim
+    j, t = 17, 5                                   # poisoned row j, fed token t != j
+    E = gm.arena[:V * d * 4].view(torch.float32)  # the embedding sits at arena offset 0
+    E[j * d + 3] = float("nan")
+    logits = torch.empty((batch, V), dtype=torch.float32, device=dev)
+    gm.decode_step(np.full(batch, t, np.int32), logits=logits)
+    assert gm.status() == LD_E_NONFINITE
+    assert gm.status() == 0                        # cleared after reporting
+    g = logits.cpu().numpy()
+    assert np.isnan(g[:, j]).all()
+    assert np.isfinite(np.delete(g, j, axis=1)).all()
+    # the prompt path (per-row classifier of each sequence's last position)
+    gm.kv_reset()
+    prompts = np.full((batch, 6), t, np.int32)
+    gm.prefill(prompts, logits=logits)
+    assert gm.status() == LD_E_NONFINITE
+    # a finite table again: no report
+    E[j * d + 3] = 0.0
+    gm.kv_reset()
+    gm.decode_step(np.full(batch, t, np.int32), logits=logits)
     assert gm.status() == 0
     gm.close()
 

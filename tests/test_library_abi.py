@@ -66,7 +66,8 @@ def _cfg(m, **kw):
                                  dict(max_seq=0), dict(max_batch=0), dict(rope_theta=0.0),
                                  dict(dim=64, n_heads=1, hidden_dim=64, vocab_size=10, max_seq=4) | {"n_layers": 0},
                                  dict(dim=512, n_heads=1), dict(n_kv_heads=3), dict(n_kv_heads=-1),
-                                 dict(weight_bf16=2), dict(max_pos=50), dict(max_pos=-1)])
+                                 dict(weight_bf16=2), dict(max_pos=50), dict(max_pos=-1),
+                                 dict(hidden_dim=39936 + 32), dict(hidden_dim=65536)])
 def test_arena_bytes_rejects_unsupported_configs(L, bad):
     n = C.c_size_t(0)
     raw = {k: bad.pop(k) for k in list(bad) if k in ("weight_bf16", "max_pos")}   # set on the C struct as is
@@ -74,6 +75,14 @@ def test_arena_bytes_rejects_unsupported_configs(L, bad):
     for k, v in raw.items():
         setattr(c, k, v)
     assert L.ld_arena_bytes(C.byref(c), C.byref(n)) == _lib.LD_E_INVAL
+
+
+def test_longest_gemv_input_is_accepted(L):
+    # the batch-1 W2 projection stages its whole input (hidden_dim floats) in LDS:
+    # 39936 floats fit beside its static arrays in gfx950's 160 KiB
+    n = C.c_size_t(0)
+    c = _cfg(TINY, hidden_dim=39936)
+    assert L.ld_arena_bytes(C.byref(c), C.byref(n)) == _lib.LD_OK and n.value > 0
 
 
 def test_arena_sizes_of_the_workloads(L):

@@ -23,8 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-I", CSRC, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "synth")]
 # no packed-fp32 instructions in any generated code
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _synth_obj():

@@ -15,7 +15,6 @@ LD_E_RANGE = -2
 LD_E_ARENA = -3
 LD_E_HIP = -4
 LD_E_NONFINITE = -5
-LD_E_STATE = -6
 
 LD_K_QKV, LD_K_ATTN, LD_K_WO, LD_K_W13, LD_K_W2, LD_K_CLS = range(6)
 

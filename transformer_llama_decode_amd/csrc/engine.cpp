@@ -47,12 +47,13 @@ size_t kv_ring(const ld_config* c) {
 int validate(const ld_config* c) {
   if (c == nullptr) return LD_E_INVAL;
   if (c->dim <= 0 || c->dim % 32 != 0 || c->dim > 16384) return LD_E_INVAL;
+  // the batch-1 GEMV stages its whole input vector (dim, or hidden_dim for W2) in LDS
   if (c->n_layers <= 0 || c->n_layers > 1024) return LD_E_INVAL;
   if (c->n_heads <= 0 || c->dim % c->n_heads != 0) return LD_E_INVAL;
   if (c->n_kv_heads < 0 || (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0)) return LD_E_INVAL;
   const int hd = c->dim / c->n_heads;
   if (hd % 16 != 0 || hd > 256) return LD_E_INVAL;
-  if (c->hidden_dim <= 0 || c->hidden_dim % 32 != 0 || c->hidden_dim > 65536) return LD_E_INVAL;
+  if (c->hidden_dim <= 0 || c->hidden_dim % 32 != 0 || c->hidden_dim > kGemvMaxK) return LD_E_INVAL;
   if (c->vocab_size <= 0 || c->vocab_size > (1 << 20)) return LD_E_INVAL;
   if (c->max_seq <= 0 || c->max_seq > (1 << 16)) return LD_E_INVAL;
   if (c->max_batch <= 0 || c->max_batch > 4096) return LD_E_INVAL;
@@ -61,6 +62,59 @@ int validate(const ld_config* c) {
   if (c->max_pos < 0 || c->max_pos > (1 << 24) || (c->max_pos > 0 && c->max_pos < c->max_seq))
     return LD_E_INVAL;
   return LD_OK;
+}
+
+// Per-pass scratch of the forward pass (everything a step writes and reads back
+// that is neither a weight, the KV cache nor a caller's output): activations,
+// attention and split-K partials with their tickets (zero between launches),
+// arg-max partials, token staging, carved from the arena.
+struct Scratch {
+  float *x, *xn, *q, *att, *g;
+  double* attn_part;
+  int* attn_ticket;
+  double* sk_ws;        // nullptr: split-K tiles stay in one workgroup
+  int* sk_ticket;
+  double* ssq;
+  float* arg_val;
+  int* arg_idx;
+  int* tok;
+  int* next;
+  int rows;             // activation rows one pass may take
+};
+
+// Scratch pointers for `rows` rows inside a region at `base`; returns the bytes
+// used.  With base == nullptr only sizes.  The tickets come first, at offsets
+// that do not depend on the model (kernels re-arm them to zero after each use,
+// so a region cleared once keeps them valid for every later pass, whatever
+// model it serves).
+size_t scratch_layout(const ld_config* c, int rows, bool split_k, char* base, Scratch* sc) {
+  const size_t d = c->dim, f = c->hidden_dim, V = c->vocab_size, hd = d / c->n_heads, R = rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += round_up(bytes, kAlign);
+    return p;
+  };
+  sc->attn_ticket = reinterpret_cast<int*>(take((size_t)kMaxAttnParts * 4));
+  sc->sk_ticket = reinterpret_cast<int*>(take((size_t)kSkMaxTiles * 4));
+  static_assert(kMaxAttnParts * 4 % kAlign == 0 && kSkMaxTiles * 4 % kAlign == 0 &&
+                    kMaxAttnParts * 4 + kSkMaxTiles * 4 == kScratchTicketBytes,
+                "tickets: the fixed front of every scratch region");
+  sc->x = reinterpret_cast<float*>(take(R * d * 4));
+  sc->xn = reinterpret_cast<float*>(take(R * d * 4));
+  sc->q = reinterpret_cast<float*>(take(R * d * 4));
+  sc->att = reinterpret_cast<float*>(take(R * d * 4));
+  sc->g = reinterpret_cast<float*>(take(R * f * 4));
+  sc->attn_part = reinterpret_cast<double*>(take((size_t)kMaxAttnParts * (hd + 2) * 8));
+  sc->sk_ws = split_k ? reinterpret_cast<double*>(take(kSkWorkspaceBytes)) : nullptr;
+  sc->ssq = reinterpret_cast<double*>(take((size_t)kSsqRows * ((d + 31) / 32) * 8));
+  const size_t arg_parts = std::max((size_t)1024, R * 4 * ((V + 127) / 128));   // up to 4 per 128 columns
+  sc->arg_val = reinterpret_cast<float*>(take(arg_parts * 4));
+  sc->arg_idx = reinterpret_cast<int*>(take(arg_parts * 4));
+  sc->tok = reinterpret_cast<int*>(take(R * 4));
+  sc->next = reinterpret_cast<int*>(take(R * 4));
+  sc->rows = rows;
+  return off;
 }
 
 void make_layout(const ld_config* c, Layout* L) {
@@ -94,21 +148,8 @@ void make_layout(const ld_config* c, Layout* L) {
   const size_t R = std::max(B, std::min((size_t)kMaxRowsCap, B * S));
   L->rows = (int)R;
   L->seq_pad = (int)Sp;
-  L->x = take(R * d * 4);
-  L->xn = take(R * d * 4);
-  L->q = take(R * d * 4);
-  L->att = take(R * d * 4);
-  L->g = take(R * f * 4);
-  L->attn_part = take((size_t)kMaxAttnParts * (hd + 2) * 8);
-  L->attn_ticket = take((size_t)kMaxAttnParts * 4);
-  L->sk_ws = take(kSkWorkspaceBytes);
-  L->sk_ticket = take((size_t)kSkMaxTiles * 4);
-  L->ssq = take((size_t)kSsqRows * ((d + 31) / 32) * 8);
-  L->arg_parts = std::max((size_t)1024, R * 4 * ((V + 127) / 128));   // up to 4 per 128 columns
-  L->arg_val = take(L->arg_parts * 4);
-  L->arg_idx = take(L->arg_parts * 4);
-  L->tok = take(R * 4);
-  L->next = take(R * 4);
+  Scratch sizes;
+  L->scratch = take(scratch_layout(c, (int)R, true, nullptr, &sizes));
   L->err = take(4);
   L->csum = take(8);
   L->pos_dev = take(2 * 4);
@@ -127,6 +168,7 @@ struct Prof {
 struct ld_model {
   ld_config c;
   Layout lay;
+  Scratch sc;            // the pass's scratch (in the arena)
   int hd, kvh, kvd, device;   // head dim, key/value heads, kvh * hd
   hipStream_t stream;
   char* arena;
@@ -362,10 +404,10 @@ int layers_gemv(ld_model* m, int pos) {
   const ld_config& c = m->c;
   const int* pos_dev = m->dev_pos ? m->at<int>(m->lay.pos_dev) : nullptr;
   const int d = c.dim, f = c.hidden_dim;
-  float* x = m->at<float>(m->lay.x);
-  float* q = m->at<float>(m->lay.q);
-  float* att = m->at<float>(m->lay.att);
-  float* g = m->at<float>(m->lay.g);
+  float* x = m->sc.x;
+  float* q = m->sc.q;
+  float* att = m->sc.att;
+  float* g = m->sc.g;
   for (int l = 0; l < c.n_layers; ++l) {
     {
       ProfScope ps(m, K_QKV, true);
@@ -383,8 +425,8 @@ int layers_gemv(ld_model* m, int pos) {
     {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
-      a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
-      a.ticket = m->at<int>(m->lay.attn_ticket);
+      a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->sc.attn_part;
+      a.ticket = m->sc.attn_ticket;
       a.rows = 1; a.n_tok = 1; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev; a.kvh = m->kvh;
       a.window = c.max_seq;
@@ -435,9 +477,9 @@ bool carried_norm(const ld_model* m, int rows) {
 // layer's carried norm reads)
 hipError_t embed_rows(ld_model* m, const int* tok, int rows, const int* pos_src, int* pos_dst) {
   const ld_config& c = m->c;
-  return launch_embed(tok, m->arena + m->lay.E, m->bf16, m->at<float>(m->lay.x), rows, c.dim, c.vocab_size,
+  return launch_embed(tok, m->arena + m->lay.E, m->bf16, m->sc.x, rows, c.dim, c.vocab_size,
                       m->at<int>(m->lay.err), pos_src, pos_dst,
-                      carried_norm(m, rows) ? m->at<double>(m->lay.ssq) : nullptr, m->stream);
+                      carried_norm(m, rows) ? m->sc.ssq : nullptr, m->stream);
 }
 
 // rows = B * n_tok rows (sequence-major) on the MFMA GEMM path.
@@ -445,13 +487,13 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
   const ld_config& c = m->c;
   const int* pos_dev = m->dev_pos ? m->at<int>(m->lay.pos_dev) : nullptr;
   const int d = c.dim, f = c.hidden_dim;
-  float* x = m->at<float>(m->lay.x);
-  float* xn = m->at<float>(m->lay.xn);
-  float* q = m->at<float>(m->lay.q);
-  float* att = m->at<float>(m->lay.att);
-  float* g = m->at<float>(m->lay.g);
+  float* x = m->sc.x;
+  float* xn = m->sc.xn;
+  float* q = m->sc.q;
+  float* att = m->sc.att;
+  float* g = m->sc.g;
   const bool cn = carried_norm(m, rows);
-  double* ssq = cn ? m->at<double>(m->lay.ssq) : nullptr;
+  double* ssq = cn ? m->sc.ssq : nullptr;
   for (int l = 0; l < c.n_layers; ++l) {
     if (!cn)
       LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->layer(l, m->lay.o_gatt), rows, d, 1, 0, c.norm_eps,
@@ -459,7 +501,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_QKV, true);
       GemmArgs a{};
-      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
+      a.ws = m->sc.sk_ws; a.tickets = m->sc.sk_ticket;
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = cn ? x : xn; a.W = m->wlayer(l, m->lay.o_wqkv); a.bf16 = m->bf16; a.M = rows; a.N = d + 2 * m->kvd;
       a.K = d; a.carry = m->carry; a.kvh = m->kvh;
@@ -475,8 +517,8 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_ATTN);
       AttnArgs a{};
-      a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->at<double>(m->lay.attn_part);
-      a.ticket = m->at<int>(m->lay.attn_ticket);
+      a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.out = att; a.part = m->sc.attn_part;
+      a.ticket = m->sc.attn_ticket;
       a.rows = rows; a.n_tok = n_tok; a.pos = pos; a.d = d; a.H = c.n_heads; a.hd = m->hd;
       a.seq_pad = m->lay.seq_pad; a.bmax = c.max_batch; a.pos_dev = pos_dev; a.kvh = m->kvh;
       a.window = c.max_seq;
@@ -485,7 +527,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_WO, true);
       GemmArgs a{};
-      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
+      a.ws = m->sc.sk_ws; a.tickets = m->sc.sk_ticket;
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = att; a.W = m->wlayer(l, m->lay.o_wo); a.bf16 = m->bf16; a.M = rows; a.N = d; a.K = d; a.carry = m->carry;
       a.resid = x; a.ssq_out = ssq;
@@ -497,7 +539,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_W13, true);
       GemmArgs a{};
-      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
+      a.ws = m->sc.sk_ws; a.tickets = m->sc.sk_ticket;
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = cn ? x : xn; a.W = m->wlayer(l, m->lay.o_w13); a.bf16 = m->bf16; a.M = rows; a.N = 2 * f; a.K = d;
       a.carry = m->carry; a.g_out = g; a.f = f;
@@ -509,7 +551,7 @@ int layers_gemm(ld_model* m, int rows, int n_tok, int pos) {
     {
       ProfScope ps(m, K_W2, true);
       GemmArgs a{};
-      a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
+      a.ws = m->sc.sk_ws; a.tickets = m->sc.sk_ticket;
       a.ev_start = ps.start(); a.ev_stop = ps.stop();
       a.A = g; a.W = m->wlayer(l, m->lay.o_w2); a.bf16 = m->bf16; a.M = rows; a.N = d; a.K = f; a.carry = m->carry;
       a.resid = x; a.ssq_out = l + 1 < c.n_layers ? ssq : nullptr;   // the next layer's Q/K/V norm
@@ -526,16 +568,16 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
          int out_row0, int* next) {
   const ld_config& c = m->c;
   const int d = c.dim, V = c.vocab_size;
-  float* x = m->at<float>(m->lay.x);
-  float* xn = m->at<float>(m->lay.xn);
-  float* pv = m->at<float>(m->lay.arg_val);
-  int* pi = m->at<int>(m->lay.arg_idx);
+  float* x = m->sc.x;
+  float* xn = m->sc.xn;
+  float* pv = m->sc.arg_val;
+  int* pi = m->sc.arg_idx;
   int* err = m->at<int>(m->lay.err);
-  int* next_int = m->at<int>(m->lay.next);
+  int* next_int = m->sc.next;
   const int cls_rows = all_pos ? B * n_tok : B;
   int nparts = 0;
   // capacity of the partial arrays (R rows x the GEMM's 2 or 4 partials per 128 columns)
-  if (cls_rows > m->lay.rows) return LD_E_ARENA;
+  if (cls_rows > m->sc.rows) return LD_E_ARENA;
   if (cls_rows == 1) {
     ProfScope ps(m, K_CLS, true);
     GemvArgs a{};
@@ -553,7 +595,7 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
       LD_TRY_HIP(launch_rmsnorm_rows(x, xn, m->at<float>(m->lay.gain_final), B, d, n_tok, n_tok - 1,
                                      c.norm_eps, m->stream));
     GemmArgs a{};
-    a.ws = m->at<double>(m->lay.sk_ws); a.tickets = m->at<int>(m->lay.sk_ticket);
+    a.ws = m->sc.sk_ws; a.tickets = m->sc.sk_ticket;
     a.A = xn; a.W = m->arena + m->lay.Wcls; a.bf16 = m->bf16; a.M = cls_rows; a.N = V; a.K = d; a.carry = m->carry;
     a.logits = logits;
     a.n_tok = all_pos ? n_tok : 1;
@@ -598,7 +640,7 @@ int build_step_graph(ld_model* m, int batch, float* dev_logits) {
     rc = LD_E_HIP;
   } else {
     int* pd = m->at<int>(m->lay.pos_dev);
-    if (embed_rows(m, m->at<int>(m->lay.next), batch, pd + 1, pd) != hipSuccess) rc = LD_E_HIP;
+    if (embed_rows(m, m->sc.next, batch, pd + 1, pd) != hipSuccess) rc = LD_E_HIP;
     if (rc == LD_OK) rc = (batch == 1) ? layers_gemv(m, 0) : layers_gemm(m, batch, 1, 0);
     if (rc == LD_OK) rc = head(m, batch, 1, false, dev_logits, 1, 0, nullptr);
     if (hipStreamEndCapture(m->cap_stream, &g) != hipSuccess && rc == LD_OK) rc = LD_E_HIP;
@@ -652,6 +694,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
   if (!m) return LD_E_INVAL;
   m->c = *cfg;
   m->lay = L;
+  scratch_layout(cfg, L.rows, true, reinterpret_cast<char*>(dev_arena) + L.scratch, &m->sc);
   m->hd = cfg->dim / cfg->n_heads;
   m->kvh = kv_heads(cfg);
   m->kvd = m->kvh * m->hd;
@@ -739,10 +782,10 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
         hipMemcpyAsync(m->at<float>(L.rope_sin), st.data(), st.size() * 4, hipMemcpyHostToDevice,
                        m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.Kc, 0, L.Vc - L.Kc, m->stream) != hipSuccess ||
-        hipMemsetAsync(m->arena + L.Vc, 0, L.x - L.Vc, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->arena + L.Vc, 0, L.scratch - L.Vc, m->stream) != hipSuccess ||
         hipMemsetAsync(m->arena + L.err, 0, 4, m->stream) != hipSuccess ||
-        hipMemsetAsync(m->arena + L.attn_ticket, 0, (size_t)kMaxAttnParts * 4, m->stream) != hipSuccess ||
-        hipMemsetAsync(m->arena + L.sk_ticket, 0, (size_t)kSkMaxTiles * 4, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->sc.attn_ticket, 0, (size_t)kMaxAttnParts * 4, m->stream) != hipSuccess ||
+        hipMemsetAsync(m->sc.sk_ticket, 0, (size_t)kSkMaxTiles * 4, m->stream) != hipSuccess ||
         hipStreamSynchronize(m->stream) != hipSuccess)
       return fail(LD_E_HIP);
   }
@@ -756,9 +799,9 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
   if (m->pos + 1 > positions(&m->c)) return LD_E_RANGE;
   if (!tokens_on_device && !tokens_valid(tokens, (size_t)batch, m->c.vocab_size)) return LD_E_INVAL;
   DeviceGuard dg(m->device);
-  const int* d_tok = tokens_on_device ? tokens : m->at<int>(m->lay.tok);
+  const int* d_tok = tokens_on_device ? tokens : m->sc.tok;
   if (!tokens_on_device) {
-    int rc = enqueue_host_tokens(m, tokens, (size_t)batch, m->at<int>(m->lay.tok));
+    int rc = enqueue_host_tokens(m, tokens, (size_t)batch, m->sc.tok);
     if (rc != LD_OK) return rc;
   }
   LD_TRY_HIP(embed_rows(m, d_tok, batch, nullptr, nullptr));
@@ -777,7 +820,7 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
   if (!tokens_valid(host_tokens, (size_t)batch * n_tokens, m->c.vocab_size)) return LD_E_INVAL;
   DeviceGuard dg(m->device);
   const ld_config& c = m->c;
-  const int R = m->lay.rows;
+  const int R = m->sc.rows;
   const int nc_max = std::max(1, R / batch);   // positions per chunk
   std::vector<int32_t> chunk_tok;
   const int pos0 = m->pos;
@@ -794,9 +837,9 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
     for (int b = 0; b < batch; ++b)
       std::memcpy(&chunk_tok[(size_t)b * nc], host_tokens + (size_t)b * n_tokens + t0,
                   sizeof(int32_t) * nc);
-    int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows, m->at<int>(m->lay.tok));
+    int rc = enqueue_host_tokens(m, chunk_tok.data(), (size_t)rows, m->sc.tok);
     if (rc != LD_OK) return rc;
-    LD_TRY_HIP(embed_rows(m, m->at<int>(m->lay.tok), rows, nullptr, nullptr));
+    LD_TRY_HIP(embed_rows(m, m->sc.tok, rows, nullptr, nullptr));
     rc = (rows == 1) ? layers_gemv(m, pos0 + t0) : layers_gemm(m, rows, nc, pos0 + t0);
     if (rc != LD_OK) return rc;
     const bool last = t0 + nc >= n_tokens;
@@ -819,7 +862,7 @@ int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* toke
   DeviceGuard dg(m->device);
   int rc = build_step_graph(m, batch, dev_logits);
   if (rc != LD_OK) return rc;
-  int* first = m->at<int>(m->lay.next);   // the graph's input tokens
+  int* first = m->sc.next;   // the graph's input tokens
   if (tokens_on_device) {
     LD_TRY_HIP(hipMemcpyAsync(first, tokens, sizeof(int32_t) * batch, hipMemcpyDeviceToDevice,
                               m->stream));
@@ -1016,7 +1059,6 @@ const char* ld_strerror(int code) {
     case LD_E_ARENA: return "arena too small or misaligned";
     case LD_E_HIP: return "HIP runtime error";
     case LD_E_NONFINITE: return "non-finite logit or out-of-range device token";
-    case LD_E_STATE: return "invalid state";
     default: return "unknown error";
   }
 }

@@ -33,6 +33,7 @@ namespace ld {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kGemvDefaultLds = 64 * 1024 - 256;   // dynamic LDS below the default limit, with the static arrays
 constexpr int kWavesPerBlock = kThreads / kWave;
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_CLS = 3 };
@@ -494,6 +495,19 @@ hipError_t launch_cfg2(const GemvArgs& a, int max_blocks, hipStream_t s, int* bl
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks_out) *blocks_out = blocks;
   const size_t shmem = (size_t)a.K * sizeof(float);
+  if (a.K > kGemvMaxK) return hipErrorInvalidValue;
+  if (shmem > (size_t)kGemvDefaultLds) {
+    // x staged whole past the default 64 KiB dynamic LDS limit (gfx950 has 160 KiB per CU);
+    // one flag per kernel instantiation
+    static bool raised = false;
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<EPI, RW, U, NT, BF, MODE, BIG>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kGemvMaxK * (int)sizeof(float));
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
   if (a.ev_start != nullptr)
     hipExtLaunchKernelGGL((k_gemv<EPI, RW, U, NT, BF, MODE, BIG>), dim3(blocks), dim3(kThreads), shmem, s,
                           a.ev_start, a.ev_stop, 0, a);

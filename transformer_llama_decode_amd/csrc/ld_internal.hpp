@@ -43,13 +43,13 @@ enum KernelClass { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_CLS =
 struct Layout {
   size_t E, Wcls, gain_final, rope_cos, rope_sin, Kc, Vc;
   size_t layer0, layer_stride, o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn;
-  size_t x, xn, q, att, g, attn_part, attn_ticket, sk_ws, sk_ticket, ssq, arg_val, arg_idx, tok, next, err;
+  size_t scratch;      // per-pass scratch region (engine.cpp: scratch_layout)
+  size_t err;
   size_t csum;         // one 64-bit accumulator of ld_weights_checksum
   size_t pos_dev, gen;
   size_t total;
   int rows;            // R: activation rows per forward pass
   int seq_pad;         // Sp
-  size_t arg_parts;    // capacity of the arg-max partial arrays
 };
 
 // ---- kernel launchers (return hipError_t of the launch) ----
@@ -82,6 +82,9 @@ struct GemvArgs {
   int* err;
 };
 
+// Longest input vector of the batch-1 GEMV: it stages x[K] whole in LDS (160 KiB
+// per CU on gfx950, 4 KiB left for the kernel's static arrays).
+constexpr int kGemvMaxK = (160 - 4) * 1024 / 4;
 hipError_t launch_gemv_qkv(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_resid(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s);
@@ -89,7 +92,7 @@ hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_cls(const GemvArgs& a, int* nparts, hipStream_t s);
 
 // Model width from which fp32 matrix-core sums no longer keep the logits within
-// tolerance on their own: the GEMMs carry their sums into fp64 every 32 k, and
+// tolerance on their own: the GEMMs carry their sums into fp64 every 8 k, and
 // prompt attention stays on the fp64 vector path.
 constexpr int kWideDim = 2048;
 
@@ -116,7 +119,7 @@ struct GemmArgs {
   const void* W;      // [N][K], fp32, or bfloat16 when bf16 (widened exactly on load)
   bool bf16;
   int M, N, K;
-  bool carry;          // fp32 MFMA partial sums carried into fp64 every 32 k
+  bool carry;          // fp32 MFMA partial sums carried into fp64 every 8 k
   hipEvent_t ev_start, ev_stop;   // when set, recorded by the dispatch itself (timing)
   // QKV epilogue
   float* q_out;
@@ -162,7 +165,10 @@ constexpr int kSsqRows = 256;   // rows the small-problem GEMM takes at most
 constexpr int kSkMaxTiles = 256;
 constexpr int kSkMaxSlices = 16;
 constexpr size_t kSkWorkspaceBytes = (size_t)16 << 20;
+// the tickets (attention, split-K) at the front of every scratch region
+constexpr int kScratchTicketBytes = kMaxAttnParts * 4 + kSkMaxTiles * 4;
 hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s);
+
 hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_cls(const GemmArgs& a, int* nparts, hipStream_t s);

@@ -76,13 +76,32 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, n_steps):
-    """The oracle (plain single-threaded C, fp64 accumulation) on this host."""
+def host_cpu():
+    """The host's CPU as lscpu reports it: model, logical CPUs, sockets, and the
+    CPUs this process may run on."""
+    import subprocess
+    info = {"model": None, "logical_cpus": os.cpu_count(), "sockets": None,
+            "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return info
+    for line in out.splitlines():
+        k, _, v = line.partition(":")
+        k, v = k.strip(), v.strip()
+        if k == "Model name" and info["model"] is None:
+            info["model"] = v
+        elif k == "Socket(s)":
+            info["sockets"] = int(v) if v.isdigit() else v
+    return info
+
+
+def _oracle_rate(L, w, n_steps, model=None):
+    """tok/s of one oracle build over positions 0..n_steps-1 of w's model from
+    token 1 (greedy), one host thread; the weights are drawn beforehand."""
     import numpy as np
     from oracle import oracle as O
-    t0 = time.time()
-    m = O.OracleModel(w.model, w.model_seed, nthreads=min(16, os.cpu_count() or 1))
-    gen_s = time.time() - t0
+    m = model or O.OracleModel(w.model, w.model_seed, nthreads=min(16, os.cpu_count() or 1), L=L)
     st = m.new_state()
     logits = np.empty(w.model.vocab_size, np.float32)
     tok = 1
@@ -90,12 +109,46 @@ def cpu_baseline(w, n_steps):
     for p in range(n_steps):
         tok, _ = m.forward(st, tok, p, logits)
     dt = time.perf_counter() - t0
+    if model is None:
+        m.close()
+    return n_steps / dt
+
+
+def cpu_baseline(w, n_steps):
+    """The oracle (plain single-threaded C) on this host: the parity build (fp64
+    accumulation) on a bounded sample of the benchmarked workload, and, for
+    comparison with the pages' CPU figures, a timing-only build with float
+    accumulators (the pages' plain fp32 loop, gcc -O3 without fast-math) on the
+    same sample and on the whole 15M-shape run (256 positions)."""
+    from oracle import oracle as O
+    from oracle import _build as OB
+    from transformer_llama_decode_amd.configs import WORKLOADS
+    if not os.path.exists(OB.ORACLE_TIMING_LIB):
+        OB.build_oracle_timing()
+    Ld, Lf = O.lib(), O.lib(OB.ORACLE_TIMING_LIB)
+    t0 = time.time()
+    m = O.OracleModel(w.model, w.model_seed, nthreads=min(16, os.cpu_count() or 1), L=Ld)
+    gen_s = time.time() - t0
+    rate = _oracle_rate(Ld, w, n_steps, model=m)
     m.close()
+    del m
+    rate_f = _oracle_rate(Lf, w, n_steps)
+    c1 = WORKLOADS["C1"]
+    c1_d = _oracle_rate(Ld, c1, c1.end_pos)
+    c1_f = _oracle_rate(Lf, c1, c1.end_pos)
     return {
-        "value": n_steps / dt, "unit": "tok/s", "cores": 1, "kind": "oracle",
+        "value": rate, "unit": "tok/s", "cores": 1, "kind": "oracle",
         "sample": "%d decode positions (p=0..%d) of the %s model, batch 1, one host thread, "
                   "gcc -O3, fp32 storage / fp64 accumulation; weights drawn beforehand in %.0fs"
                   % (n_steps, n_steps - 1, w.name, gen_s),
+        "float_accumulation": {
+            "value": rate_f, "unit": "tok/s", "cores": 1,
+            "sample": "the same %d positions, oracle built with -DOR_ACC=float (timing only)" % n_steps},
+        "c1_15m_shape": {
+            "fp64_accumulation_tok_s": c1_d, "float_accumulation_tok_s": c1_f, "cores": 1,
+            "sample": "C1: positions 0..%d of the 15M shape from token 1 (the pages quote ~100 tok/s "
+                      "for this shape on one M1 core)" % (c1.end_pos - 1)},
+        "host": host_cpu(),
     }
 
 
@@ -230,6 +283,8 @@ def main():
                          "HIP graph) instead of one ld_decode_step call per position (both feed "
                          "the greedy tokens back on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="with the default workload, skip the other configurations' sub-records")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("DIR", "WORKLOAD"),
@@ -254,7 +309,6 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -274,15 +328,48 @@ def main():
         return
 
     from transformer_llama_decode_amd.configs import WORKLOADS
-    from transformer_llama_decode_amd.model import LlamaDecoder, synth_prompt
-    from transformer_llama_decode_amd import _lib
 
     w = WORKLOADS[args.workload]
+    rec = measure(w, args.steps, args.warmup, args.graph)
+    if args.workload == "C5" and not args.no_others:
+        # the other configurations of the metric, each over (up to) its first
+        # decode positions: the 15M / 44M / 110M batch-1 shapes and the two
+        # batched-decode shapes (matrix-core projections)
+        rec["other_workloads"] = {}
+        for name, steps in [("C1", 255), ("C2", 512), ("C4", 512), ("C3", 240), ("C4b32", 512)]:
+            r = measure(WORKLOADS[name], steps, 16, args.graph)
+            rec["other_workloads"][name] = {
+                k: r[k] for k in ("value", "unit", "ms_per_step", "hbm_gbps_step", "hbm_frac_step", "prefill_ms")}
+            rec["other_workloads"][name]["positions"] = r["config"]["positions"]
+            rec["other_workloads"][name]["batch"] = r["config"]["batch"]
+            if r["roofline"]["bound"] == "mfma":
+                rec["other_workloads"][name]["mfma"] = {
+                    k: r["roofline"][k] for k in ("achieved", "peak", "unit", "frac", "whole_step_frac",
+                                                  "gemm_ms_per_step", "per_class_ms")}
+        rec["batched"] = dict(rec["other_workloads"]["C3"], workload="C3: 15M shape, 256 sequences in lockstep")
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline: drawing weights for the oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+def measure(w, n_steps, warmup, graph):
+    """Init, prefill (timed on its own), `warmup` untimed decode steps, then
+    exactly n_steps timed decode steps at positions P .. P+n_steps-1 (P = the
+    prompt length), tokens fed back on the device; then the same positions again
+    with HIP event pairs around the projection kernels.  Returns the JSON record."""
+    import numpy as np
+    import torch
+    from transformer_llama_decode_amd.model import LlamaDecoder, synth_prompt
+    from transformer_llama_decode_amd import _lib
     cfg = w.model
     B = w.batch
     P = max(w.prompt_len, 1)
-    steps = min(args.steps, w.end_pos - P)
-    if P + max(steps, args.warmup) > cfg.positions:
+    steps = min(n_steps, w.end_pos - P)
+    if P + max(steps, warmup) > cfg.positions:
         sys.exit("steps + prompt exceed the model's %d positions" % cfg.positions)
     dev = torch.device("cuda", 0)
     t0 = time.time()
@@ -313,15 +400,15 @@ def main():
             tok = out
         return tok
 
-    gen_out = torch.empty((max(steps, args.warmup), B), dtype=torch.int32, device=dev)
+    gen_out = torch.empty((max(steps, warmup), B), dtype=torch.int32, device=dev)
 
     def run_timed(k, tok):
-        if not args.graph:
+        if not graph:
             return run(k, tok)
         gm.generate(tok, k, out=gen_out)
         return gen_out[k - 1]
 
-    tok = run_timed(args.warmup, bufs[0]) if args.warmup > 0 else bufs[0]
+    tok = run_timed(warmup, bufs[0]) if warmup > 0 else bufs[0]
     torch.cuda.synchronize()
     gm.set_pos(P)                      # time exactly the workload's positions P .. P+steps-1
     start_tok = tok.clone()
@@ -407,7 +494,7 @@ def main():
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -421,7 +508,7 @@ def main():
             "prompt_tokens": int(prompt.shape[1]) if w.prompt_len else 0,
             "seed": w.model_seed,
             "weights": "bf16" if cfg.weight_bf16 else "f32",
-            "loop": ("ld_generate: one HIP graph replay per position" if args.graph else
+            "loop": ("ld_generate: one HIP graph replay per position" if graph else
                      "ld_decode_step per position, tokens fed back on the device"),
         },
         "hbm_gbps_step": round(avg_bytes * tok_s / B / 1e9, 1),
@@ -435,12 +522,9 @@ def main():
     gm.close()
     del gm
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        log("cpu baseline: drawing weights for the oracle ...")
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
-    else:
-        rec["cpu_baseline"] = None
-    print(json.dumps(rec), flush=True)
+    return rec
+
+
 
 
 if __name__ == "__main__":

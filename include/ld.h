@@ -48,6 +48,11 @@ extern "C" {
 #define LD_E_ARENA -3     /* arena too small or misaligned */
 #define LD_E_HIP -4       /* a HIP runtime call failed */
 #define LD_E_NONFINITE -5 /* a logit was NaN or infinite, or a device token was out of range */
+#define LD_E_SCRATCH -6   /* ld_decode_step_noalloc: the step needs more than LD_STATIC_SCRATCH_BYTES */
+
+/* Bytes of the library's static device scratch array (one per GPU; see
+ * ld_decode_step_noalloc). */
+#define LD_STATIC_SCRATCH_BYTES (32u << 20)
 
 typedef struct {
   int32_t dim;             /* model width d; multiple of 32, at most 16384 */
@@ -123,6 +128,25 @@ int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host
  * if pos + 1 > max_pos. */
 int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
                    float* dev_logits, int32_t* dev_next);
+
+/* For callers that cannot allocate device memory or must not touch the arena's
+ * scratch (code under HIP graph capture, serving loops that forbid allocation):
+ * ld_decode_step, same arguments and results (bit for bit), with the step's
+ * scratch -- activations, attention and split-K partials and their tickets,
+ * arg-max partials, token staging -- in the library's static device array of
+ * LD_STATIC_SCRATCH_BYTES instead of the arena's scratch region.  Each GPU holds
+ * one copy of that array until the process ends; ld_model_init resolves it for
+ * its device.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine).  LD_E_SCRATCH (nothing done) when the step needs more than the array
+ * holds: the activations of `batch` rows, 2 KiB + 8 * (head_dim + 2) KiB of
+ * attention partials, 16 MiB of split-K partials when batch > 1, and the
+ * arg-max partials (batch * 4 * ceil(vocab / 128) values, at least 1024) -- for
+ * example batch 1 of the 7B shape needs about 1.3 MiB.  Every caller on one GPU
+ * shares its copy, which keeps the last call's contents: calls that overlap on
+ * one GPU (other streams, other threads, other handles) race.  Under capture,
+ * pass device tokens (host tokens are staged with an event wait). */
+int ld_decode_step_noalloc(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
+                           float* dev_logits, int32_t* dev_next);
 
 /* Greedy generation on the device: n_steps decode positions for `batch`
  * sequences, each step's arg-max token fed back as the next step's input with

@@ -16,7 +16,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libld.so")
 ARCH = "gfx950"
 
-KERNELS = ["k_gemv.hip", "k_attn.hip", "k_attn_prefill.hip", "k_gemm.hip", "k_misc.hip"]
+KERNELS = ["k_gemv.hip", "k_attn.hip", "k_attn_prefill.hip", "k_gemm.hip", "k_misc.hip", "static_scratch.hip"]
 HOST = ["engine.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

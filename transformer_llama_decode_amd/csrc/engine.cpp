@@ -67,7 +67,8 @@ int validate(const ld_config* c) {
 // Per-pass scratch of the forward pass (everything a step writes and reads back
 // that is neither a weight, the KV cache nor a caller's output): activations,
 // attention and split-K partials with their tickets (zero between launches),
-// arg-max partials, token staging, carved from the arena.
+// arg-max partials, token staging.  Normally carved from the arena; the
+// allocation-free entry point swaps in the library's static device array.
 struct Scratch {
   float *x, *xn, *q, *att, *g;
   double* attn_part;
@@ -168,7 +169,7 @@ struct Prof {
 struct ld_model {
   ld_config c;
   Layout lay;
-  Scratch sc;            // the pass's scratch (in the arena)
+  Scratch sc;            // the pass's scratch: the arena's, or the static array's for one call
   int hd, kvh, kvd, device;   // head dim, key/value heads, kvh * hd
   hipStream_t stream;
   char* arena;
@@ -789,6 +790,8 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
         hipStreamSynchronize(m->stream) != hipSuccess)
       return fail(LD_E_HIP);
   }
+  // this GPU's copy of the static scratch array (ld_decode_step_noalloc), once per device
+  if (static_scratch_setup(m->device, m->stream) != hipSuccess) return fail(LD_E_HIP);
   *out = m;
   return LD_OK;
 }
@@ -811,6 +814,23 @@ int ld_decode_step(ld_model* m, int32_t batch, const int32_t* tokens, int32_t to
   if (rc != LD_OK) return rc;
   m->pos += 1;
   return LD_OK;
+}
+
+int ld_decode_step_noalloc(ld_model* m, int32_t batch, const int32_t* tokens, int32_t tokens_on_device,
+                           float* dev_logits, int32_t* dev_next) {
+  if (!m || !tokens || batch <= 0 || batch > m->c.max_batch) return LD_E_INVAL;
+  char* base = static_scratch(m->device);
+  if (base == nullptr) return LD_E_HIP;   // set up by ld_model_init on this device
+  Scratch sc;
+  // the same layout as the arena's scratch, sized for this call's rows (the
+  // split-K workspace only when the projections are GEMMs)
+  if (scratch_layout(&m->c, batch, batch > 1, nullptr, &sc) > kStaticScratchBytes) return LD_E_SCRATCH;
+  scratch_layout(&m->c, batch, batch > 1, base, &sc);
+  const Scratch saved = m->sc;
+  m->sc = sc;
+  const int rc = ld_decode_step(m, batch, tokens, tokens_on_device, dev_logits, dev_next);
+  m->sc = saved;
+  return rc;
 }
 
 int ld_prefill(ld_model* m, int32_t batch, int32_t n_tokens, const int32_t* host_tokens,
@@ -1059,6 +1079,7 @@ const char* ld_strerror(int code) {
     case LD_E_ARENA: return "arena too small or misaligned";
     case LD_E_HIP: return "HIP runtime error";
     case LD_E_NONFINITE: return "non-finite logit or out-of-range device token";
+    case LD_E_SCRATCH: return "the call needs more scratch than the library's static device array holds";
     default: return "unknown error";
   }
 }

@@ -169,6 +169,16 @@ constexpr size_t kSkWorkspaceBytes = (size_t)16 << 20;
 constexpr int kScratchTicketBytes = kMaxAttnParts * 4 + kSkMaxTiles * 4;
 hipError_t launch_gemm_qkv(const GemmArgs& a, hipStream_t s);
 
+// The library's own scratch for callers that cannot allocate (static_scratch.hip):
+// kStaticScratchBytes per GPU, whose first kScratchTicketBytes (the tickets of
+// every scratch region) are zero between passes.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static_assert(kStaticScratchBytes == LD_STATIC_SCRATCH_BYTES, "the header states the size");
+// Once per device, with `device` current: resolve this GPU's copy of the array
+// and clear its tickets (synchronous on s).  Later calls return at once.
+hipError_t static_scratch_setup(int device, hipStream_t s);
+// The device address of `device`'s copy, or nullptr before its set-up.
+char* static_scratch(int device);
 hipError_t launch_gemm_resid(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_cls(const GemmArgs& a, int* nparts, hipStream_t s);

@@ -84,6 +84,24 @@ class LlamaDecoder:
                                     nxt.data_ptr()), "ld_decode_step")
         return nxt
 
+    def decode_step_noalloc(self, tokens, logits=None, next_out=None):
+        """decode_step with the step's scratch in the library's static device array
+        (ld_decode_step_noalloc).  Returns the status code (LD_OK, or LD_E_SCRATCH
+        when the step needs more than the array holds) and the next-token tensor."""
+        torch = self.torch
+        if isinstance(tokens, torch.Tensor) and tokens.is_cuda:
+            assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+            B, ptr, on_dev = tokens.numel(), tokens.data_ptr(), 1
+            keep = None
+        else:
+            keep = np.ascontiguousarray(np.atleast_1d(tokens), dtype=np.int32)
+            B, ptr, on_dev = keep.size, keep.ctypes.data, 0
+        nxt = next_out if next_out is not None else self.next[:B]
+        rc = self.L.ld_decode_step_noalloc(self._h, B, ptr, on_dev,
+                                           logits.data_ptr() if logits is not None else None,
+                                           nxt.data_ptr())
+        return rc, nxt
+
     def generate(self, tokens, n_steps, logits=None, out=None):
         """Greedy on-device generation of n_steps positions (one HIP graph replay each).
 

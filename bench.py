@@ -154,7 +154,7 @@ def cpu_baseline(w, n_steps):
 
 def counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """The rocprofv3 passes a traffic summary comes from (each counter in a run of its own)."""
-    run = "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline"
+    run = "python -u bench.py --steps 16 --warmup 2 --no-cpu-baseline --no-others"
     cal = "python -u bench.py --copy-calibration"
     return ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o f -- %s" % (fetch_dir, run),
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o w -- %s" % (write_dir, run),
@@ -196,8 +196,10 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out
         if name not in write:
             continue
         t = fetch[name] * k_fetch + write[name] * k_write
-        alg = w13_launch_bytes(cfg) if name.startswith("k_gemv<2,") else None
-        if name.startswith("k_gemv<2,"):
+        # the 7B W1/W3 GEMV: the SwiGLU epilogue (2) with streamed loads, the largest of them
+        is_w13 = name.startswith("k_gemv<2,") and w13 is None
+        alg = w13_launch_bytes(cfg) if is_w13 else None
+        if is_w13:
             w13 = t
         lines.append("%-28s %14.1f %14.1f %22.0f %18s" % (name, fetch[name] / 1024, write[name] / 1024, t,
                                                            alg if alg else "-"))
@@ -216,6 +218,28 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out
                  "-> scale fetch x%.4f, write x%.4f\n" % (f_copy / 1024, w_copy / 1024, k_fetch, k_write))
         fh.write("\n".join(lines) + "\n")
     print(json.dumps(rec))
+
+
+def summarize_trace(trace_dir, title, command, out_txt):
+    """Per-kernel durations of one rocprofv3 --kernel-trace --stats run (its
+    *_kernel_stats.csv) as a text table under profiles/."""
+    import csv
+    import glob
+    import re
+    path = glob.glob(os.path.join(trace_dir, "*_kernel_stats.csv"))[0]
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["%-52s %7s %12s %10s %10s %10s" % ("kernel", "calls", "total_ms", "avg_us", "min_us", "max_us")]
+    for r in rows:
+        name = re.sub(r"^void ", "", r["Name"]).replace("ld::(anonymous namespace)::", "").replace("ld::", "")
+        lines.append("%-52s %7d %12.3f %10.2f %10.2f %10.2f" % (
+            name[:52], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    with open(out_txt, "w") as fh:
+        fh.write("rocprofv3 kernel statistics: %s\n\ncommand (from the repository root, on an MI355X):\n  %s\n  "
+                 "python bench.py --summarize-trace %s '<title>' %s\n\n" % (title, command, trace_dir, out_txt))
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE"
@@ -257,7 +281,7 @@ def summarize_mfma(pmc_dir, workload, out_txt, n_xcd=8, n_simd=1024):
                  "prompt's prefill: the LDS-tiled k_gemm launches with few calls).\n"
                  "command (from the repository root, on an MI355X):\n"
                  "  rocprofv3 --pmc %s --output-format csv -d %s -o m -- python -u bench.py --workload %s "
-                 "--steps 16 --warmup 2 --no-cpu-baseline\n"
+                 "--steps 16 --warmup 2 --no-cpu-baseline --no-others\n"
                  "  python bench.py --summarize-mfma %s %s\n\n"
                  % (workload, MFMA_COUNTERS, pmc_dir, workload, pmc_dir, workload))
         fh.write("\n".join(lines) + "\n")
@@ -290,6 +314,8 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("DIR", "WORKLOAD"),
                     help="a rocprofv3 --pmc run of the MFMA counters on a batched workload: writes "
                          "the matrix-core use per kernel under profiles/")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("DIR", "TITLE", "COMMAND", "OUT"),
+                    help="a rocprofv3 --kernel-trace --stats output dir: writes its per-kernel table to OUT")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
                     help="rocprofv3 --pmc output dirs: FETCH_SIZE and WRITE_SIZE of this bench, "
                          "then of --copy-calibration; writes the traffic summary under profiles/")
@@ -297,6 +323,9 @@ def main():
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma[0], args.summarize_mfma[1],
                        os.path.join(ROOT, "profiles", "mfma_%s.txt" % args.summarize_mfma[1].lower()))
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, TRAFFIC_FILE,

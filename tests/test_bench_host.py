@@ -78,3 +78,45 @@ def test_mfma_summary_from_counters(tmp_path):
     assert float(line[-3]) == pytest.approx(512e6)      # flops per call
     assert "k_fill" not in text                          # no matrix-core work, no line
     assert "all matrix-core kernels: MFMA busy 25.0%" in text
+
+
+def test_trace_summary_table(tmp_path):
+    cols = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
+    with open(tmp_path / "x_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=cols)
+        w.writeheader()
+        w.writerow(dict(zip(cols, ["void ld::(anonymous namespace)::k_small(int)", 4, 8000, 2000, 1, 1500, 2500, 1])))
+        w.writerow(dict(zip(cols, ["void ld::(anonymous namespace)::k_big(ld::GemvArgs)", 2, 100000, 50000, 99, 49000,
+                                   51000, 1])))
+    out = tmp_path / "t.txt"
+    bench.summarize_trace(str(tmp_path), "a title", "rocprofv3 ...", str(out))
+    text = out.read_text().splitlines()
+    assert text[0].startswith("rocprofv3 kernel statistics: a title")
+    body = [ln for ln in text if ln.startswith("k_")]
+    assert body[0].split()[0] == "k_big(GemvArgs)" and body[1].split()[0] == "k_small(int)"   # by total time
+    assert body[0].split()[1:4] == ["2", "0.100", "50.00"]
+
+
+def test_w13_traffic_is_taken_from_the_streamed_7b_kernel(tmp_path):
+    # two W1/W3 instantiations (the 7B one streams 360 MB, a small model's 6 MB):
+    # the summary must report the 7B one
+    big = "void ld::(anonymous namespace)::k_gemv<2, 1, 4, true, false, 0, true>(ld::GemvArgs)"
+    small = "void ld::(anonymous namespace)::k_gemv<2, 1, 4, false, false, 0, false>(ld::GemvArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    dirs = {k: tmp_path / k for k in ("f", "w", "cf", "cw")}
+    for d in dirs.values():
+        d.mkdir()
+    kib = 1024.0
+    _write_pmc_csv(dirs["f"] / "f_counter_collection.csv",
+                   [(1, big, "FETCH_SIZE", 360786944 / 2 / kib, 0, 1), (2, small, "FETCH_SIZE", 6e6 / 2 / kib, 0, 1)])
+    _write_pmc_csv(dirs["w"] / "w_counter_collection.csv",
+                   [(1, big, "WRITE_SIZE", 0.0, 0, 1), (2, small, "WRITE_SIZE", 0.0, 0, 1)])
+    _write_pmc_csv(dirs["cf"] / "f_counter_collection.csv", [(1, copy, "FETCH_SIZE", (4 << 29) / 2 / kib, 0, 1)])
+    _write_pmc_csv(dirs["cw"] / "w_counter_collection.csv", [(1, copy, "WRITE_SIZE", (4 << 29) / kib, 0, 1)])
+    out_json, out_txt = tmp_path / "t.json", tmp_path / "t.txt"
+    bench.summarize_counters(str(dirs["f"]), str(dirs["w"]), str(dirs["cf"]), str(dirs["cw"]), str(out_json),
+                             str(out_txt))
+    import json
+    rec = json.loads(out_json.read_text())
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["bytes_per_launch"] == 360786944

@@ -33,6 +33,19 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// floor(f / n) for f * n < 2^24 (staging slots: f < 2^13, n <= 80; head and row
+// indices: f < 2^14, n <= 256): f * ceil(2^24 / n)
+// >> 24, one multiply-high instead of the ~35-instruction sequence of a division
+// by a run-time value (which every staging slot otherwise pays, on a cold
+// instruction cache at each launch).  Exact because the reciprocal's rounding
+// adds less than f / 2^24 < 1 / n to the quotient.
+struct FastDiv {
+  uint32_t mul;
+  int n;
+  __device__ __forceinline__ explicit FastDiv(int n_) : mul((16777216u + (uint32_t)n_ - 1u) / (uint32_t)n_), n(n_) {}
+  __device__ __forceinline__ int div(int f) const { return (int)__umulhi((uint32_t)f << 8, mul); }
+};
+
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_CLS = 3 };
 
 constexpr int BK = 32;   // K step of the tiled kernel (64 for the few-row classifier)
@@ -340,7 +353,6 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   constexpr int NACC = BN / 32;                  // 32 x 32 accumulators per wave
   constexpr int TE = NACC * 1024;                // elements of the output tile
   constexpr int ROWS = 32 + BN;                  // staged rows: 32 of A, BN of W
-  constexpr int PER_THREAD = (ROWS * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS;   // float4 slots
   static_assert(BN == 32 || BN == 64, "tile width");
   static_assert(EPI != EPI_SWIGLU || BN == 64, "SwiGLU pairs W1 and W3 blocks of 32 rows in one tile");
   static_assert(EPI != EPI_CLS || BN == 64, "arg-max partials: one lane per column of a 64-wide tile");
@@ -357,6 +369,12 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   const int ldsw = kc + 4;   // LDS row stride: a 16-byte skew from row to row
   const int row = lane & 31, kofs = 4 * (lane >> 5);
 
+  // Every global load below is unconditional, at an index clamped into the
+  // tensor: a load under a per-lane condition becomes a branch that hipcc closes
+  // with a wait for memory, which turned the staging of one K chunk into one
+  // round trip per slot.  Clamped rows (past M or N) and the slots past the chunk
+  // load valid data that no stored output depends on.
+
   // operands the epilogue reads, fetched now so they arrive during the K loop:
   // residual elements (thread handles outputs e = tid + i * SK_THREADS) and the
   // rotary cos / sin of its q / k pairs (pairs e = tid + i * SK_THREADS)
@@ -366,22 +384,24 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   if (EPI == EPI_RESID) {
 #pragma unroll
     for (int i = 0; i < RES_PER; ++i) {
-      const int e = tid + i * SK_THREADS, r = m0 + e / BN, c = n0 + e % BN;
-      res_in[i] = (r < M && c < N) ? a.resid[(size_t)r * N + c] : 0.f;
+      const int e = tid + i * SK_THREADS, r = min(m0 + e / BN, M - 1), c = min(n0 + e % BN, N - 1);
+      res_in[i] = a.resid[(size_t)r * N + c];   // used only for r < M, c < N
     }
   }
+  // run-time divisors of the Q/K/V epilogue (head dim, positions per sequence)
+  const FastDiv div_hd(EPI == EPI_QKV ? a.hd : 1), div_tok(EPI == EPI_QKV ? a.n_tok : 1);
   if (EPI == EPI_QKV) {
     const int d = a.d, hd = a.hd, half = hd >> 1;
 #pragma unroll
     for (int i = 0; i < PAIR_PER; ++i) {
-      const int e = tid + i * SK_THREADS, r = m0 + e / (BN / 2), col = n0 + 2 * (e % (BN / 2));
-      rc_in[i] = 1.f;
-      rs_in[i] = 0.f;
-      if (r < M && col < N && col < d + a.kvh * hd) {
-        const int ii = (col % d) % hd, b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
-        rc_in[i] = a.rcos[p * half + (ii >> 1)];
-        rs_in[i] = a.rsin[p * half + (ii >> 1)];
-      }
+      // used only for rows < M and query / key columns
+      const int e = tid + i * SK_THREADS, r = min(m0 + e / (BN / 2), M - 1);
+      const int col = min(n0 + 2 * (e % (BN / 2)), N - 2);
+      int c;
+      qkv_section(col, d, a.kvh * hd, &c);
+      const int ii = c - div_hd.div(c) * hd, b = div_tok.div(r), p = pos0 + (r - b * a.n_tok);
+      rc_in[i] = a.rcos[p * half + (ii >> 1)];
+      rs_in[i] = a.rsin[p * half + (ii >> 1)];
     }
   }
 
@@ -396,46 +416,50 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
   for (int j = 0; j < (CARRY ? 16 : 1); ++j) dacc[0][j] = dacc[1][j] = 0.0;
 
   // RMSNorm applied while staging A (Q/K/V and SwiGLU when norm_gain is set):
-  // the A slots (the first G_SLOTS of each thread) also fetch the gains of their
-  // columns, and each of the 32 rows' scale comes from its sums of squares
+  // the A slots also fetch the gains of their columns, and each of the 32 rows'
+  // scale comes from its sums of squares
   constexpr bool CAN_NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU;
   const bool nrm = CAN_NORM && a.norm_gain != nullptr;
-  constexpr int G_SLOTS = CAN_NORM ? (32 * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS : 1;
   __shared__ double inv_s[32];
-  float4 gst[G_SLOTS];
 
-  // one chunk [kb, kb + kn) of the ROWS staged rows, flat float4 index f = r * (kn/4) + c
-  float4 st[PER_THREAD];
+  // one chunk [kb, kb + kn): the 32 A rows in slots sa (flat float4 index
+  // f = r * (kn/4) + c), the BN W rows in slots sw
+  constexpr int A_SLOTS = (32 * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS;
+  constexpr int W_SLOTS = (BN * SK_KC / 4 + SK_THREADS - 1) / SK_THREADS;
+  float4 sa[A_SLOTS], sw[W_SLOTS], gst[CAN_NORM ? A_SLOTS : 1];
+  const float* gsrc = nrm ? a.norm_gain : a.A;   // gains, or any valid address
   auto gload = [&](int kb, int kn) {
+    const FastDiv fd(kn >> 2);
     const int f4 = kn >> 2;
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int f = tid + i * SK_THREADS;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (f < ROWS * f4) {
-        const int r = f / f4, c = f - r * f4;
-        if (r < 32) {
-          if (m0 + r < M) v = *reinterpret_cast<const float4*>(a.A + (size_t)(m0 + r) * K + kb + 4 * c);
-          if (CAN_NORM && i < G_SLOTS && nrm)
-            gst[i < G_SLOTS ? i : 0] = *reinterpret_cast<const float4*>(a.norm_gain + kb + 4 * c);
-        } else if (n0 + r - 32 < N) {
-          v = load_w4<BF>(a.W, (size_t)(n0 + r - 32) * K + kb + 4 * c);
-        }
-      }
-      st[i] = v;
+    for (int i = 0; i < A_SLOTS; ++i) {
+      int f = tid + i * SK_THREADS;
+      f = f < 32 * f4 ? f : 0;
+      const int r = fd.div(f), c = f - r * f4;
+      sa[i] = *reinterpret_cast<const float4*>(a.A + (size_t)min(m0 + r, M - 1) * K + kb + 4 * c);
+      if (CAN_NORM) gst[CAN_NORM ? i : 0] = *reinterpret_cast<const float4*>(gsrc + kb + 4 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < W_SLOTS; ++i) {
+      int f = tid + i * SK_THREADS;
+      f = f < BN * f4 ? f : 0;
+      const int r = fd.div(f), c = f - r * f4;
+      sw[i] = load_w4<BF>(a.W, (size_t)min(n0 + r, N - 1) * K + kb + 4 * c);
     }
   };
   auto sstore = [&](int kn) {
+    const FastDiv fd(kn >> 2);
     const int f4 = kn >> 2;
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
+    for (int i = 0; i < A_SLOTS; ++i) {
       const int f = tid + i * SK_THREADS;
-      if (f < ROWS * f4) {
-        const int r = f / f4, c = f - r * f4;
-        float4 v = st[i];
-        if (CAN_NORM && i < G_SLOTS && nrm && r < 32) {
+      if (f < 32 * f4) {
+        const int r = fd.div(f), c = f - r * f4;
+        float4 v = sa[i];
+        if (CAN_NORM && nrm) {
+          // rows past M have scale 0 (their loads are of a valid row)
           const double inv = inv_s[r];
-          const float4 g = gst[i < G_SLOTS ? i : 0];
+          const float4 g = gst[CAN_NORM ? i : 0];
           v.x = (float)((double)v.x * inv * (double)g.x);
           v.y = (float)((double)v.y * inv * (double)g.y);
           v.z = (float)((double)v.z * inv * (double)g.z);
@@ -444,27 +468,33 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
         *reinterpret_cast<float4*>(stg + r * ldsw + 4 * c) = v;
       }
     }
+#pragma unroll
+    for (int i = 0; i < W_SLOTS; ++i) {
+      const int f = tid + i * SK_THREADS;
+      if (f < BN * f4) {
+        const int r = fd.div(f), c = f - r * f4;
+        *reinterpret_cast<float4*>(stg + (32 + r) * ldsw + 4 * c) = sw[i];
+      }
+    }
   };
 
   gload(kbeg, min(kc, kend - kbeg));
-  if (nrm && tid < 32) {
-    // 1 / sqrt(mean square + eps) of row m0 + tid, its d / 32 group sums added in order
+  if (nrm) {
+    // 1 / sqrt(mean square + eps) of row m0 + tid / 16: its d / 32 group sums, 16
+    // lanes each taking groups j, j + 16, ..., then a fixed butterfly over the 16
     // (the loop's first barrier publishes it before the first staging)
-    const int r = m0 + tid, nps = K / 32;
-    double inv = 0.0;
-    if (r < M) {
-      const double* p = a.ssq_in + (size_t)r * nps;
-      double ss = 0.0;
-      for (int g0 = 0; g0 < nps; g0 += 8) {
-        double v[8];
+    const int rl = tid >> 4, part = tid & 15, nps = K / 32;
+    const double* p = a.ssq_in + (size_t)min(m0 + rl, M - 1) * nps;
+    double ss = 0.0;
+    for (int g0 = part; g0 < nps; g0 += 16 * 8) {
+      double v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = g0 + u < nps ? p[g0 + u] : 0.0;
+      for (int u = 0; u < 8; ++u) v[u] = p[min(g0 + 16 * u, nps - 1)];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ss += v[u];
-      }
-      inv = 1.0 / sqrt(ss / (double)K + a.norm_eps);
+      for (int u = 0; u < 8; ++u) ss += g0 + 16 * u < nps ? v[u] : 0.0;
     }
-    inv_s[tid] = inv;
+    ss = group_sum<16>(ss);
+    if (part == 0) inv_s[rl] = m0 + rl < M ? 1.0 / sqrt(ss / (double)K + a.norm_eps) : 0.0;
   }
   for (int kb = kbeg; kb < kend; kb += kc) {
     const int kn = min(kc, kend - kb);
@@ -578,8 +608,8 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
       if (r >= M || col >= N) continue;
       float y0 = tile(rl, cl), y1 = tile(rl, cl + 1);
       int c;
-      const int sec = qkv_section(col, d, a.kvh * hd, &c), h = c / hd, ii = c - h * hd;
-      const int b = r / a.n_tok, p = pos0 + (r - b * a.n_tok);
+      const int sec = qkv_section(col, d, a.kvh * hd, &c), h = div_hd.div(c), ii = c - h * hd;
+      const int b = div_tok.div(r), p = pos0 + (r - b * a.n_tok);
       if (sec < 2) rope_pair(y0, y1, rc_in[i], rs_in[i], y0, y1);
       const size_t head_off = ((size_t)b * a.kvh + h) * (size_t)a.seq_pad * hd;   // k, v
       if (sec == 0) {

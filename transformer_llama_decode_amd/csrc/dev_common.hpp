@@ -9,13 +9,45 @@ namespace ld {
 
 constexpr int kWave = 64;
 
-// Butterfly sum across the 64 lanes; every lane ends with the same value and the
-// order of additions is fixed, so results are run-to-run identical.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// One DPP data movement of a double (both 32-bit halves moved alike).  Lanes of
+// rows outside ROWS (a 4-bit mask of 16-lane rows) receive `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v, double old) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned long long o = __builtin_bit_cast(unsigned long long, old);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp((int)(unsigned)o, (int)(unsigned)u, CTRL, ROWS, 0xf, false);
+  const unsigned hi =
+      (unsigned)__builtin_amdgcn_update_dpp((int)(unsigned)(o >> 32), (int)(unsigned)(u >> 32), CTRL, ROWS, 0xf, false);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Reductions across the 64 lanes on DPP row operations (a data path of the VALU,
+// not the LDS crossbar that a general shuffle takes): pairs within quads, the
+// half-row and row mirrors (every lane then holds its 16-lane row's result), row
+// 0's last lane into row 1 and row 2's into row 3, then row 1's into rows 2 and
+// 3; lane 63 ends with the whole wave's result, which is broadcast.  The order
+// of the additions is fixed, so results are run-to-run identical.
+template <bool MAX>
+__device__ __forceinline__ double wave_reduce(double v) {
+  const double id = MAX ? -INFINITY : 0.0;
+  auto op = [](double a, double b) { return MAX ? fmax(a, b) : a + b; };
+  v = op(v, dpp_f64<0xB1, 0xf>(v, id));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_f64<0x4E, 0xf>(v, id));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_f64<0x141, 0xf>(v, id));   // row_half_mirror
+  v = op(v, dpp_f64<0x140, 0xf>(v, id));   // row_mirror
+  v = op(v, dpp_f64<0x142, 0xa>(v, id));   // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_f64<0x143, 0xc>(v, id));   // row_bcast:31 into rows 2 and 3
+  return readlane_f64(v, 63);
+}
+
+__device__ __forceinline__ double wave_sum(double v) { return wave_reduce<false>(v); }
 
 // The same butterfly within each aligned group of W lanes (W a power of two <= 64).
 template <int W>
@@ -25,11 +57,7 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
-  return v;
-}
+__device__ __forceinline__ double wave_max(double v) { return wave_reduce<true>(v); }
 
 // (value, index) arg-max step: larger value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {

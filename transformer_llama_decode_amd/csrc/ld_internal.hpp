@@ -163,7 +163,7 @@ bool gemm_small_path(int M, int N);
 constexpr int kSsqRows = 256;   // rows the small-problem GEMM takes at most
 // capacity of the split-K workspace: tiles that may be split, slices per tile, bytes
 constexpr int kSkMaxTiles = 256;
-constexpr int kSkMaxSlices = 16;
+constexpr int kSkMaxSlices = 8;
 constexpr size_t kSkWorkspaceBytes = (size_t)16 << 20;
 // the tickets (attention, split-K) at the front of every scratch region
 constexpr int kScratchTicketBytes = kMaxAttnParts * 4 + kSkMaxTiles * 4;

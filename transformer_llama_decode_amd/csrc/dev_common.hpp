@@ -49,11 +49,18 @@ __device__ __forceinline__ double wave_reduce(double v) {
 
 __device__ __forceinline__ double wave_sum(double v) { return wave_reduce<false>(v); }
 
-// The same butterfly within each aligned group of W lanes (W a power of two <= 64).
+// The sum within each aligned group of W lanes (W a power of two <= 64), every
+// lane of the group ending with it: DPP within 16-lane rows (pairs in quads, the
+// half-row and row mirrors), then one shuffle per further doubling.  Fixed order.
 template <int W>
 __device__ __forceinline__ double group_sum(double v) {
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "power-of-two group");
+  v += dpp_f64<0xB1, 0xf>(v, 0.0);                      // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_f64<0x4E, 0xf>(v, 0.0);    // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_f64<0x141, 0xf>(v, 0.0);   // row_half_mirror
+  if constexpr (W >= 16) v += dpp_f64<0x140, 0xf>(v, 0.0);  // row_mirror
 #pragma unroll
-  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  for (int off = 16; off < W; off <<= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
@@ -67,9 +74,23 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   }
 }
 
-// Arg-max across lanes whose ids differ only in the bits of `mask_bits` (xor pattern).
+// One DPP step of the (value, index) arg-max: merge with the lane CTRL selects.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+  const float v2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+  const int i2 = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
+  argmax_merge(v, i, v2, i2);
+}
+
+// Arg-max within each aligned group of `width` lanes (16, 32 or 64): DPP within
+// 16-lane rows, then a shuffle per further doubling.  The result is the same in
+// any order (largest value, lowest index on ties).
 __device__ __forceinline__ void wave_argmax(float& v, int& i, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) {
+  argmax_dpp<0xB1>(v, i);    // quad_perm [1,0,3,2]
+  argmax_dpp<0x4E>(v, i);    // quad_perm [2,3,0,1]
+  argmax_dpp<0x141>(v, i);   // row_half_mirror
+  argmax_dpp<0x140>(v, i);   // row_mirror
+  for (int off = 16; off < width; off <<= 1) {
     float v2 = __shfl_xor(v, off, kWave);
     int i2 = __shfl_xor(i, off, kWave);
     argmax_merge(v, i, v2, i2);

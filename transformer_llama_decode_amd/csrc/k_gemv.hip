@@ -212,6 +212,30 @@ __device__ __forceinline__ void fma_batch(const T (&w)[U][NR], const float4* xs4
   }
 }
 
+// The one batch of a row of at most U * 64 weight vectors (KV of them): slots
+// past the row load its last vector (unpredicated, so all loads share one round
+// trip) and take zero weights.
+template <int NR, int U, bool NT, typename T>
+__device__ __forceinline__ void load_batch_rag(T (&w)[U][NR], const T* (&rows)[NR], int lane, int KV) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = min(u * kWave + lane, KV - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[u][r] = ld_w<NT>(rows[r] + j);
+  }
+}
+template <int NR, int U, typename T>
+__device__ __forceinline__ void fma_batch_rag(const T (&w)[U][NR], const float4* xs4, int lane, int KV,
+                                              double (&acc)[NR]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = u * kWave + lane;
+    const auto xv = ld_x(xs4, min(j, KV - 1), T{});
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = dotw(j < KV ? w[u][r] : T{}, xv, acc[r]);
+  }
+}
+
 // acc[r] += sum over this lane's slice of K of W_r . x  for NR row pointers,
 // starting at weight vector block `it` (the blocks before it are done already);
 // KV = weight vectors (16 bytes each) per row.
@@ -279,11 +303,14 @@ __device__ __forceinline__ double pick(const double (&acc)[N], int i) {
 //              reduction and epilogue, so the memory pipe stays busy across groups;
 //  MODE_DB     rows of exactly one batch (64 * U vectors): two batch buffers,
 //              group g+1's loads are issued before group g's products, so two
-//              groups are in flight per wave.
-enum Mode { MODE_PLAIN = 0, MODE_PIPE = 1, MODE_DB = 2 };
+//              groups are in flight per wave;
+//  MODE_DBR    as MODE_DB for rows of at most one batch (64 * (U-1) < KV <= 64 * U):
+//              short rows (small models) then cost one round trip, issued before
+//              the prologue, where the block-by-block walk took two or three.
+enum Mode { MODE_PLAIN = 0, MODE_PIPE = 1, MODE_DB = 2, MODE_DBR = 3 };
 
-// BIG: rows of at least one batch (U * 64 weight vectors); the first batch is
-// then loaded before the prologue.  Shorter rows (small models) skip it.
+// BIG: the first batch is loaded before the prologue (rows of at least one batch
+// of U * 64 weight vectors, or MODE_DBR's single ragged batch).
 template <int EPI, int RW, int U, bool NT, bool BF, int MODE, bool BIG>
 __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   static_assert(EPI != EPI_QKV || RW % 2 == 0, "a rotary pair's two rows sit in one row group");
@@ -300,6 +327,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * RW : RW;
   const int ngroups = (N + RW - 1) / RW;
   const int wstride = gridDim.x * kWavesPerBlock;
+  constexpr bool DB = MODE == MODE_DB || MODE == MODE_DBR, RAG = MODE == MODE_DBR;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   bool nonfinite = false;
@@ -332,13 +360,18 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
     // arrive, waiting for HBM right here): a wave without a group loads rows
     // that exist (set_rows clamps them) and does not use them
     pre = grp < ngroups;
+    if constexpr (RAG) {
+      load_batch_rag<NR, U, NT>(wpre, rows, lane, KV);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) wpre[u][r] = ld_w<NT>(rows[r] + u * kWave + lane);
+        for (int r = 0; r < NR; ++r) wpre[u][r] = ld_w<NT>(rows[r] + u * kWave + lane);
+    }
   }
-  // x float4 per thread loaded at once (W2's input is the FFN width)
-  constexpr int XB = !BIG ? 2 : (EPI == EPI_RESID) ? 12 : 8;
+  // x float4 per thread loaded at once (W2's input is the FFN width; short rows:
+  // at most 512 float4)
+  constexpr int XB = (!BIG || RAG) ? 2 : (EPI == EPI_RESID) ? 12 : 8;
   XStage<XB> xr;
   stage_issue<XB, EPI != EPI_RESID>(xr, a.x, a.gain, K);
 
@@ -421,14 +454,15 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
     }
   };
 
-  if constexpr (MODE == MODE_DB) {
+  if constexpr (DB) {
     // every row is one batch: buffers wpre (group g) and wnx (group g + wstride)
     T wnx[U][NR];
     auto group = [&](int g, const T (&w)[U][NR], const EpiIn& e) {
       double acc[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[r] = 0.0;
-      fma_batch<NR, U>(w, xs4, 0, lane, acc);
+      if constexpr (RAG) fma_batch_rag<NR, U>(w, xs4, lane, KV, acc);
+      else fma_batch<NR, U>(w, xs4, 0, lane, acc);
       finish(g * RW, acc, e);
     };
     for (; grp < ngroups; grp += 2 * wstride) {
@@ -436,14 +470,16 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       const EpiIn e0 = fetch_epi(grp * RW);   // before the next loads: waited for without them
       if (g1 < ngroups) {
         set_rows(rows, g1 * RW);
-        load_batch<NR, U, NT>(wnx, rows, 0, lane);
+        if constexpr (RAG) load_batch_rag<NR, U, NT>(wnx, rows, lane, KV);
+        else load_batch<NR, U, NT>(wnx, rows, 0, lane);
       }
       group(grp, wpre, e0);
       if (g1 >= ngroups) break;
       const EpiIn e1 = fetch_epi(g1 * RW);
       if (g2 < ngroups) {
         set_rows(rows, g2 * RW);
-        load_batch<NR, U, NT>(wpre, rows, 0, lane);
+        if constexpr (RAG) load_batch_rag<NR, U, NT>(wpre, rows, lane, KV);
+        else load_batch<NR, U, NT>(wpre, rows, 0, lane);
       }
       group(g1, wnx, e1);
     }
@@ -519,7 +555,7 @@ hipError_t launch_cfg2(const GemvArgs& a, int max_blocks, hipStream_t s, int* bl
 template <int EPI, int RW, int U, bool NT, bool BF, int MODE>
 hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blocks_out) {
   if (a.K / WVec<BF>::E / kWave >= U) return launch_cfg2<EPI, RW, U, NT, BF, MODE, true>(a, max_blocks, s, blocks_out);
-  if constexpr (MODE == MODE_DB) return hipErrorInvalidValue;   // rows of exactly one batch
+  if constexpr (MODE == MODE_DB || MODE == MODE_DBR) return hipErrorInvalidValue;   // rows of one batch
   else return launch_cfg2<EPI, RW, U, NT, BF, MODE, false>(a, max_blocks, s, blocks_out);
 }
 
@@ -527,11 +563,31 @@ hipError_t launch_cfg(const GemvArgs& a, int max_blocks, hipStream_t s, int* blo
 // in the Infinity Cache from one token to the next.
 bool streamed(const GemvArgs& a) { return a.stream; }
 
+constexpr int kMaxBlocks = 512;   // 2 resident workgroups per CU on 256 CUs; the grid strides beyond
+
+// fp32 rows of at most 8 blocks of 64 vectors (K <= 2048: small models): one
+// batch of U = the row's block count (rounded up to 1, 2, 3, 4, 6 or 8) per row
+template <int EPI, int RW, bool NT>
+hipError_t launch_short(const GemvArgs& a, hipStream_t s, int* blocks_out) {
+  const int nb = (a.K / 4 + kWave - 1) / kWave;
+  if (nb <= 1) return launch_cfg2<EPI, RW, 1, NT, false, MODE_DBR, true>(a, kMaxBlocks, s, blocks_out);
+  if (nb <= 2) return launch_cfg2<EPI, RW, 2, NT, false, MODE_DBR, true>(a, kMaxBlocks, s, blocks_out);
+  if (nb <= 3) return launch_cfg2<EPI, RW, 3, NT, false, MODE_DBR, true>(a, kMaxBlocks, s, blocks_out);
+  if (nb <= 4) return launch_cfg2<EPI, RW, 4, NT, false, MODE_DBR, true>(a, kMaxBlocks, s, blocks_out);
+  if (nb <= 6) return launch_cfg2<EPI, RW, 6, NT, false, MODE_DBR, true>(a, kMaxBlocks, s, blocks_out);
+  return launch_cfg2<EPI, RW, 8, NT, false, MODE_DBR, true>(a, kMaxBlocks, s, blocks_out);
+}
+constexpr int kShortRowMaxK = 8 * kWave * 4;
+
 template <int EPI, int RW, int U, bool BF>
 hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
-  constexpr int kMaxBlocks = 512;   // 2 resident workgroups per CU on 256 CUs; the grid strides beyond
   if (a.bf16 != BF || a.K % WVec<true>::E != 0) return hipErrorInvalidValue;   // whole 16-byte vectors
-  if constexpr (!BF) {   // fp32 rows hold several batches; the plain walk measured best
+  if constexpr (!BF) {
+    if (a.K <= kShortRowMaxK) {   // short rows: one batch per row, double-buffered
+      if (streamed(a)) return launch_short<EPI, RW, true>(a, s, blocks_out);
+      return launch_short<EPI, RW, false>(a, s, blocks_out);
+    }
+    // longer fp32 rows hold several batches; the plain walk measured best
     if (streamed(a)) return launch_cfg<EPI, RW, U, true, BF, MODE_PLAIN>(a, kMaxBlocks, s, blocks_out);
     return launch_cfg<EPI, RW, U, false, BF, MODE_PLAIN>(a, kMaxBlocks, s, blocks_out);
   } else {

@@ -157,8 +157,9 @@ int ld_decode_step_noalloc(ld_model* m, int32_t batch, const int32_t* tokens, in
  * ld_decode_step).  Step i's tokens go to dev_out[i * batch + b] (device
  * memory, n_steps * batch ints, NULL = not written); dev_logits[batch][V]
  * receives the logits of every step in turn, so it ends with the last step's
- * (NULL = not written).  The step is captured once as a HIP graph per (batch,
- * dev_logits) and replayed; a different pair recaptures it.  Same results as
+ * (NULL = not written).  The step is captured once per (batch, dev_logits), as a
+ * HIP graph of one step and one of 8 consecutive steps, and replayed (the 8-step
+ * graph while 8 or more steps are left); a different pair recaptures them.  Same results as
  * n calls of ld_decode_step fed with their own dev_next, up to the rounding
  * of the attention split (fixed here by the cache size rather than the position).
  * Then pos += n_steps.  LD_E_RANGE if pos + n_steps > max_pos; n_steps == 0

@@ -1,4 +1,4 @@
-"""On-device greedy generation (ld_generate: one HIP graph replay per position).
+"""On-device greedy generation (ld_generate: HIP graphs of 8 steps, then of one step, replayed).
 
 The generated tokens are checked against the oracle teacher-forced with those
 same tokens: at every position the GPU's token must be the oracle's arg-max

@@ -27,6 +27,7 @@ namespace {
 constexpr int kMaxRowsCap = 4096;     // activation rows per forward pass (prefill is chunked)
 constexpr int kTokSlots = 4;          // pinned host slots for host token ids
 constexpr int kProfPairs = 1 << 15;   // event pairs per profiled kernel class
+constexpr int kGraphSteps = 8;        // decode steps per graph launch of ld_generate
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -187,6 +188,7 @@ struct ld_model {
   bool dev_pos;            // launches read the position from device memory (while capturing)
   hipStream_t cap_stream;  // private stream the step is captured on
   hipGraphExec_t gexec;    // replayable step, for (g_batch, g_logits)
+  hipGraphExec_t gexec_n;  // kGraphSteps consecutive steps, for the same (g_batch, g_logits)
   int g_batch;
   float* g_logits;
 
@@ -626,12 +628,9 @@ int head(ld_model* m, int B, int n_tok, bool all_pos, float* logits, int out_row
 // back as the following step's input, appends them to the token ring and
 // advances the pending position.  Replaying the graph n times decodes n
 // positions with no host work per step.
-int build_step_graph(ld_model* m, int batch, float* dev_logits) {
-  if (m->gexec != nullptr && m->g_batch == batch && m->g_logits == dev_logits) return LD_OK;
-  if (m->gexec != nullptr) {
-    LD_TRY_HIP(hipGraphExecDestroy(m->gexec));
-    m->gexec = nullptr;
-  }
+// `steps` consecutive decode steps captured into one graph: each step reads its
+// position and input tokens where the previous one left them on the device.
+int capture_steps(ld_model* m, int batch, float* dev_logits, int steps, hipGraphExec_t* exec) {
   hipStream_t user = m->stream;
   m->stream = m->cap_stream;
   m->dev_pos = true;
@@ -641,23 +640,43 @@ int build_step_graph(ld_model* m, int batch, float* dev_logits) {
     rc = LD_E_HIP;
   } else {
     int* pd = m->at<int>(m->lay.pos_dev);
-    if (embed_rows(m, m->sc.next, batch, pd + 1, pd) != hipSuccess) rc = LD_E_HIP;
-    if (rc == LD_OK) rc = (batch == 1) ? layers_gemv(m, 0) : layers_gemm(m, batch, 1, 0);
-    if (rc == LD_OK) rc = head(m, batch, 1, false, dev_logits, 1, 0, nullptr);
+    for (int i = 0; i < steps && rc == LD_OK; ++i) {
+      if (embed_rows(m, m->sc.next, batch, pd + 1, pd) != hipSuccess) rc = LD_E_HIP;
+      if (rc == LD_OK) rc = (batch == 1) ? layers_gemv(m, 0) : layers_gemm(m, batch, 1, 0);
+      if (rc == LD_OK) rc = head(m, batch, 1, false, dev_logits, 1, 0, nullptr);
+    }
     if (hipStreamEndCapture(m->cap_stream, &g) != hipSuccess && rc == LD_OK) rc = LD_E_HIP;
   }
   m->dev_pos = false;
   m->stream = user;
-  if (rc == LD_OK && hipGraphInstantiate(&m->gexec, g, nullptr, nullptr, 0) != hipSuccess) {
-    m->gexec = nullptr;
+  if (rc == LD_OK && hipGraphInstantiate(exec, g, nullptr, nullptr, 0) != hipSuccess) {
+    *exec = nullptr;
     rc = LD_E_HIP;
   }
   if (g != nullptr) (void)hipGraphDestroy(g);
-  if (rc == LD_OK) {
-    m->g_batch = batch;
-    m->g_logits = dev_logits;
-  }
   return rc;
+}
+
+int build_step_graph(ld_model* m, int batch, float* dev_logits) {
+  if (m->gexec != nullptr && m->g_batch == batch && m->g_logits == dev_logits) return LD_OK;
+  for (hipGraphExec_t* e : {&m->gexec, &m->gexec_n}) {
+    if (*e != nullptr) {
+      LD_TRY_HIP(hipGraphExecDestroy(*e));
+      *e = nullptr;
+    }
+  }
+  int rc = capture_steps(m, batch, dev_logits, 1, &m->gexec);
+  if (rc == LD_OK) rc = capture_steps(m, batch, dev_logits, kGraphSteps, &m->gexec_n);
+  if (rc != LD_OK) {
+    for (hipGraphExec_t* e : {&m->gexec, &m->gexec_n}) {
+      if (*e != nullptr) (void)hipGraphExecDestroy(*e);
+      *e = nullptr;
+    }
+    return rc;
+  }
+  m->g_batch = batch;
+  m->g_logits = dev_logits;
+  return LD_OK;
 }
 
 bool tokens_valid(const int32_t* t, size_t n, int V) {
@@ -716,6 +735,7 @@ int ld_model_init(const ld_config* cfg, uint64_t seed, void* dev_arena, size_t a
   m->dev_pos = false;
   m->cap_stream = nullptr;
   m->gexec = nullptr;
+  m->gexec_n = nullptr;
   m->g_batch = 0;
   m->g_logits = nullptr;
   if (hipGetDevice(&m->device) != hipSuccess) {
@@ -891,7 +911,10 @@ int ld_generate(ld_model* m, int32_t batch, int32_t n_steps, const int32_t* toke
     if (rc != LD_OK) return rc;
   }
   LD_TRY_HIP(launch_set_int(m->at<int>(m->lay.pos_dev) + 1, m->pos, m->stream));
-  for (int i = 0; i < n_steps; ++i) LD_TRY_HIP(hipGraphLaunch(m->gexec, m->stream));
+  // whole graphs of kGraphSteps steps, then single steps
+  int left = n_steps;
+  for (; left >= kGraphSteps; left -= kGraphSteps) LD_TRY_HIP(hipGraphLaunch(m->gexec_n, m->stream));
+  for (; left > 0; --left) LD_TRY_HIP(hipGraphLaunch(m->gexec, m->stream));
   if (dev_out != nullptr)
     LD_TRY_HIP(hipMemcpyAsync(dev_out, m->at<int>(m->lay.gen) + (size_t)m->pos * batch,
                               sizeof(int32_t) * (size_t)n_steps * batch, hipMemcpyDeviceToDevice,
@@ -1067,6 +1090,7 @@ void ld_model_free(ld_model* m) {
   for (auto& p : m->prof)
     for (auto& e : p.ev) hipEventDestroy(e);
   if (m->gexec) hipGraphExecDestroy(m->gexec);
+  if (m->gexec_n) hipGraphExecDestroy(m->gexec_n);
   if (m->cap_stream) hipStreamDestroy(m->cap_stream);
   delete m;
 }

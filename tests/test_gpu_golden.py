@@ -177,9 +177,5 @@ def test_golden_C5_bfloat16():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.xfail(strict=False, reason=(
-    "7B shape past max_seq: at the last position of the 1024-token windowed prompt "
-    "(chunked prefill) 2 of 32000 logits exceed max(1e-4|o|, 1e-5), worst by 5% "
-    "(gpu 0.0854890645, oracle 0.0854785591); later positions not yet checked"))
 def test_golden_C5_window_past_max_seq():
     _run("C5w")

@@ -104,8 +104,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   constexpr int KQ = TileRegs<HD>::KQ, DPL = TileRegs<HD>::DPL;
   constexpr int hd = HD;
   __shared__ float4 qs4[kMaxHd / 4];
-  __shared__ double sp[4][kTile];
-  __shared__ double es[kTile];
+  __shared__ double sp[2][4][kTile];   // by tile parity: one barrier per tile
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = r / a.n_tok, t = r - b * a.n_tok;
   // key/value head of query head h (grouped-query attention: H / kvh query heads share one)
@@ -146,7 +145,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
   // would spill, so they load it after
   constexpr bool kPrefetch = HD <= 128;
   TileRegs<HD> nxt;
-  for (int tile = c; tile < ntiles; tile += nchunk) {
+  for (int tile = c, par = 0; tile < ntiles; tile += nchunk, par ^= 1) {
     const int j0 = tile * kTile;
     if constexpr (kPrefetch)
       if (tile + nchunk < ntiles) load_tile<HD>(nxt, kt, vb, tile + nchunk, w, lane, fetch_len);
@@ -161,19 +160,19 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
       s4[2] = fma((double)qv.z, (double)cur.k[i].z, s4[2]);
       s4[3] = fma((double)qv.w, (double)cur.k[i].w, s4[3]);
     }
-    sp[w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    // sp[par] was last read two tiles ago, before the barrier of the tile in between
+    sp[par][w][lane] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     __syncthreads();
-    // ---- online softmax (every wave derives the same m, l from the same scores)
+    // ---- online softmax (every wave derives the same m, l and weights from the same scores)
     const bool valid = j0 + lane < kvlen && kr.visible(j0 + lane, q, lo_q);
-    const double sc = (((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane]) / sqrt_hd;
+    const double sc = (((sp[par][0][lane] + sp[par][1][lane]) + sp[par][2][lane]) + sp[par][3][lane]) / sqrt_hd;
     const double m_new = fmax(m_run, wave_max(valid ? sc : -INFINITY));
     // 0 on the first tile with a visible key (m_run = -inf); 1 while none was visible
     const double scale = m_new == -INFINITY ? 1.0 : exp(m_run - m_new);
     const double e = valid ? exp(sc - m_new) : 0.0;
-    if (w == 0) es[lane] = e;
     l_run = l_run * scale + wave_sum(e);
-    __syncthreads();
-    // ---- weighted values of this wave's 16 positions
+    // ---- weighted values of this wave's 16 positions (their weights read from the
+    // wave's own lanes 16w .. 16w + 15)
     double oo[DPL][2];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
@@ -182,7 +181,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
     }
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const double ej = es[16 * w + jj];   // 0 past the history
+      const double ej = readlane_f64(e, 16 * w + jj);   // 0 past the history
 #pragma unroll
       for (int k = 0; k < DPL; ++k) oo[k][jj & 1] = fma(ej, (double)cur.v[jj][k], oo[k][jj & 1]);
     }
@@ -194,7 +193,6 @@ __device__ __forceinline__ void attn_unit(const AttnArgs a, int c, int h, int r,
         cur = nxt;
       else
         load_tile<HD>(cur, kt, vb, tile + nchunk, w, lane, fetch_len);
-      __syncthreads();   // sp / es are rewritten by the next tile
     }
   }
 

@@ -354,6 +354,11 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   const T* rows[NR];
   set_rows(rows, grp * RW);
   T wpre[U][NR];
+  // fp32 rows longer than 2048 (at least 2 U blocks): a second batch goes out
+  // before the prologue too, so the loads in flight cover the whole prologue
+  constexpr bool PRE2 = BIG && MODE == MODE_PLAIN && !RAG && !BF;
+  static_assert(!PRE2 || 2 * U * kWave * 4 <= 2048, "two batches fit in every row that is not short");
+  T wpre2[PRE2 ? U : 1][NR];
   bool pre = false;
   if constexpr (BIG) {
     // unpredicated (a branch would make the compiler copy the registers as they
@@ -367,6 +372,12 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) wpre[u][r] = ld_w<NT>(rows[r] + u * kWave + lane);
+      if constexpr (PRE2) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) wpre2[u][r] = ld_w<NT>(rows[r] + (U + u) * kWave + lane);
+      }
     }
   }
   // x float4 per thread loaded at once (W2's input is the FFN width; short rows:
@@ -380,6 +391,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   const int pos = (EPI == EPI_QKV && a.pos_dev != nullptr) ? *a.pos_dev : a.pos;
   stage_finish<XB>(xs, xr, a.x, a.gain, K, a.eps, red);
   if constexpr (BIG) hold_batch<NR, U>(wpre);
+  if constexpr (PRE2) hold_batch<NR, U>(wpre2);
   const float4* xs4 = reinterpret_cast<const float4*>(xs);
 
   // Lane i finishes row r0 + i.  What its epilogue reads (the residual element,
@@ -495,6 +507,12 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       if ((first || MODE == MODE_PIPE) && pre) {
         fma_batch<NR, U>(wpre, xs4, 0, lane, acc);
         it0 = U;
+        if constexpr (PRE2) {
+          if (first) {
+            fma_batch<NR, U>(wpre2, xs4, U, lane, acc);
+            it0 = 2 * U;
+          }
+        }
       }
       dot_rows<NR, U, NT, MODE == MODE_PIPE>(rows, xs4, KV, lane, acc, it0);
       if (MODE == MODE_PIPE) {

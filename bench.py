@@ -537,7 +537,7 @@ def measure(w, n_steps, warmup, graph):
             "prompt_tokens": int(prompt.shape[1]) if w.prompt_len else 0,
             "seed": w.model_seed,
             "weights": "bf16" if cfg.weight_bf16 else "f32",
-            "loop": ("ld_generate: one HIP graph replay per position" if graph else
+            "loop": ("ld_generate: HIP graphs of 8 decode steps replayed" if graph else
                      "ld_decode_step per position, tokens fed back on the device"),
         },
         "hbm_gbps_step": round(avg_bytes * tok_s / B / 1e9, 1),

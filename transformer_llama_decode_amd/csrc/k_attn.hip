@@ -124,9 +124,7 @@ __global__ void __launch_bounds__(kThreads) k_attn(AttnArgs a, int nchunk) {
   }
   __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
   __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(a.ticket + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              nreal - 1;
+  if (threadIdx.x == 0) is_last = take_ticket(a.ticket + unit, nreal);
   __syncthreads();
   if (!is_last) return;
   merge_unit(pu, nreal, HD, out);

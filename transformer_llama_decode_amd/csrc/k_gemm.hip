@@ -551,9 +551,7 @@ __global__ void __launch_bounds__(SK_THREADS) k_gemm_sk(GemmArgs a, int kc, int 
     __shared__ int is_last;
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
-    if (tid == 0)
-      is_last = __hip_atomic_fetch_add(a.tickets + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                ks - 1;
+    if (tid == 0) is_last = take_ticket(a.tickets + tile_id, ks);
     __syncthreads();
     if (!is_last) return;
     // the last slice: sum the ks partials of every element in slice order

@@ -346,10 +346,10 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
     }
   };
 
-  // The weights do not depend on the input vector: issue the first batch of
-  // this wave's loads before staging (and normalising) x, then every x and gain
-  // load at once, so the prologue costs one round trip, overlapped with the
-  // batch's.
+  // The weights do not depend on the input vector: the first batch of this
+  // wave's loads is issued next to the x and gain loads (all at once), so the
+  // prologue that stages (and normalises) x costs one round trip, overlapped
+  // with the batch's.
   int grp = blockIdx.x * kWavesPerBlock + wave;
   const T* rows[NR];
   set_rows(rows, grp * RW);
@@ -360,6 +360,20 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   static_assert(!PRE2 || 2 * U * kWave * 4 <= 2048, "two batches fit in every row that is not short");
   T wpre2[PRE2 ? U : 1][NR];
   bool pre = false;
+  // x float4 per thread loaded at once (W2's input is the FFN width; short rows:
+  // at most 512 float4)
+  constexpr int XB = (!BIG || RAG) ? 2 : (EPI == EPI_RESID) ? 12 : 8;
+  XStage<XB> xr;
+  // Short rows (small models): x and the gains go out first and the single
+  // weight batch after them, so the prologue waits for x alone (loads return in
+  // order; 110M shape 0.318 -> 0.303 ms per step).  Long rows keep the batch first
+  // (7B: 4.78 -> 4.80 ms with x first), where the batch is what keeps the memory
+  // pipe busy while the prologue runs.
+  constexpr bool kXFirst = MODE == MODE_DBR;
+  if constexpr (kXFirst) {
+    stage_issue<XB, EPI != EPI_RESID>(xr, a.x, a.gain, K);
+    __asm__ volatile("" ::: "memory");   // every x load goes out before the weights
+  }
   if constexpr (BIG) {
     // unpredicated (a branch would make the compiler copy the registers as they
     // arrive, waiting for HBM right here): a wave without a group loads rows
@@ -380,11 +394,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       }
     }
   }
-  // x float4 per thread loaded at once (W2's input is the FFN width; short rows:
-  // at most 512 float4)
-  constexpr int XB = (!BIG || RAG) ? 2 : (EPI == EPI_RESID) ? 12 : 8;
-  XStage<XB> xr;
-  stage_issue<XB, EPI != EPI_RESID>(xr, a.x, a.gain, K);
+  if constexpr (!kXFirst) stage_issue<XB, EPI != EPI_RESID>(xr, a.x, a.gain, K);
 
   // position of the token (rotary angle, KV-cache slot); first needed by the
   // first row group's epilogue fetch, so the load overlaps the prologue
@@ -597,8 +607,9 @@ hipError_t launch_short(const GemvArgs& a, hipStream_t s, int* blocks_out) {
 }
 constexpr int kShortRowMaxK = 8 * kWave * 4;
 
+// max_blocks: grid cap for fp32 rows longer than kShortRowMaxK (the grid strides beyond)
 template <int EPI, int RW, int U, bool BF>
-hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
+hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr, int max_blocks = kMaxBlocks) {
   if (a.bf16 != BF || a.K % WVec<true>::E != 0) return hipErrorInvalidValue;   // whole 16-byte vectors
   if constexpr (!BF) {
     if (a.K <= kShortRowMaxK) {   // short rows: one batch per row, double-buffered
@@ -606,8 +617,8 @@ hipError_t launch(const GemvArgs& a, hipStream_t s, int* blocks_out = nullptr) {
       return launch_short<EPI, RW, false>(a, s, blocks_out);
     }
     // longer fp32 rows hold several batches; the plain walk measured best
-    if (streamed(a)) return launch_cfg<EPI, RW, U, true, BF, MODE_PLAIN>(a, kMaxBlocks, s, blocks_out);
-    return launch_cfg<EPI, RW, U, false, BF, MODE_PLAIN>(a, kMaxBlocks, s, blocks_out);
+    if (streamed(a)) return launch_cfg<EPI, RW, U, true, BF, MODE_PLAIN>(a, max_blocks, s, blocks_out);
+    return launch_cfg<EPI, RW, U, false, BF, MODE_PLAIN>(a, max_blocks, s, blocks_out);
   } else {
     // bfloat16 rows are half as many bytes: keep loads in flight across row groups
     if (a.K / WVec<BF>::E == kWave * U) {
@@ -650,7 +661,12 @@ hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s) {
 }
 hipError_t launch_gemv_cls(const GemvArgs& a, int* nparts, hipStream_t s) {
   if (a.bf16) return launch<EPI_CLS, kBfRwCls, 8, true>(a, s, nparts);
-  return launch<EPI_CLS, 2, 4, false>(a, s, nparts);   // 86.0 -> 84.7 us at the 7B shape
+  if (a.K <= kShortRowMaxK) return launch<EPI_CLS, 2, 4, false>(a, s, nparts);
+  // long rows: 86.0 -> 84.7 us at the 7B shape with batches of 4 loads; then one row
+  // per wave on 500 workgroups (16 rows per wave): 83.8 / 82.0 -> 81.0 / 79.5 us
+  // against two rows per wave on 512 (whose last grid stride left 1664 of 2048
+  // waves busy)
+  return launch<EPI_CLS, 1, 4, false>(a, s, nparts, 500);
 }
 
 }  // namespace ld

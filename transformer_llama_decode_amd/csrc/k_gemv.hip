@@ -77,22 +77,23 @@ __device__ __forceinline__ XVec8f ld_x(const float4* xs4, int j, uint4) {
 __device__ __forceinline__ double dotw(const float4 w, const XVec4& x, double acc) {
   return dot4(w, x.v[0], x.v[1], x.v[2], x.v[3], acc);
 }
-// bfloat16 weights: the 8 products of one 16-byte vector are summed in an fp32
-// chain, then carried into the fp64 accumulator.  (A bfloat16 x fp32 product has
-// up to 32 significant bits, so it is not exact in fp32: the chain's error is at
-// most ~8 units in the last place of its magnitude, ~5e-7 relative, two orders
-// below the logits' tolerance; converting every weight to fp64 instead measured
-// 3-35% slower per projection.)
+// bfloat16 weights: the products of one 16-byte vector are summed pairwise in
+// fp32 (a product and one fma), and each pair is carried into the fp64
+// accumulator.  (A bfloat16 x fp32 product has up to 32 significant bits, so it
+// is not exact in fp32: a pair's error is at most ~2 units in the last place of
+// its magnitude.  Chains of all 8 products, ~8 units, left the 7B shape's logits
+// at 1.015x the tolerance on 1 of 32000 at one decode position (worst 0.67x with
+// pairs, 0.62x with every product in fp64); pairs cost 1.6% of the bfloat16 7B
+// step against chains of 8, and every product in fp64 14%.)
 __device__ __forceinline__ double dotw(const uint4 w, const XVec8f& x, double acc) {
-  float c = bf16_lo(w.x) * x.v[0];
-  c = fmaf(bf16_hi(w.x), x.v[1], c);
-  c = fmaf(bf16_lo(w.y), x.v[2], c);
-  c = fmaf(bf16_hi(w.y), x.v[3], c);
-  c = fmaf(bf16_lo(w.z), x.v[4], c);
-  c = fmaf(bf16_hi(w.z), x.v[5], c);
-  c = fmaf(bf16_lo(w.w), x.v[6], c);
-  c = fmaf(bf16_hi(w.w), x.v[7], c);
-  return acc + (double)c;
+  const float c0 = fmaf(bf16_hi(w.x), x.v[1], bf16_lo(w.x) * x.v[0]);
+  const float c1 = fmaf(bf16_hi(w.y), x.v[3], bf16_lo(w.y) * x.v[2]);
+  const float c2 = fmaf(bf16_hi(w.z), x.v[5], bf16_lo(w.z) * x.v[4]);
+  const float c3 = fmaf(bf16_hi(w.w), x.v[7], bf16_lo(w.w) * x.v[6]);
+  acc += (double)c0;
+  acc += (double)c1;
+  acc += (double)c2;
+  return acc + (double)c3;
 }
 
 // Staging x[0..K) into LDS (with a gain: RMSNorm(x) * gain rounded to fp32), in
